@@ -1,0 +1,188 @@
+/*
+ * moe.h - C ABI of the fused FP8 x FP4 top-k Mixture-of-Experts layer for one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (pages: "MegaMoE" study notes, section "Dispatch阶段" and its flow
+ * chart; "MonoMoe kernel — design" §1):
+ *   route      top-k of softmax or sigmoid scores over E experts, optional
+ *              renormalisation of the k weights
+ *   bucketize  counting sort of the T*k (token, slot) pairs into per-expert
+ *              contiguous segments: count, prefix sum, scatter of t*k + j
+ *              ("05.10 Counting Sort / Bucketization", sections 2.1-2.3)
+ *   quant      x BF16 -> FP8 E4M3 + one UE8M0 scale per 32 hidden elements
+ *   GEMM1      per expert: rows x [W1; W3]^T, FP4 E2M1 weights with one UE8M0
+ *              scale per 32 along K, FP32 accumulation; epilogue
+ *              h = silu(gate) * up * topk_weight re-quantised to FP8 + UE8M0
+ *   GEMM2      per expert: h x W2^T (FP4), FP32 accumulation -> BF16 rows
+ *   combine    y[t] = BF16(sum over the token's k rows in FP32, slot order)
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are device memory owned by the caller; the
+ *     library never allocates, frees or keeps them.  Work is enqueued on the
+ *     given HIP stream; no call synchronises with the host.  Results are valid
+ *     once the stream has reached the call.
+ *   - Return 0 on success or a negative MOE_E* code.  Argument errors are
+ *     detected on the host before anything is enqueued.  A kernel launch error
+ *     returns MOE_EHIP; moe_error_string(MOE_EHIP) then holds the HIP message
+ *     of the calling thread's last failure.
+ *   - BF16 tensors are passed as uint16_t bit patterns, FP8/FP4 codes and
+ *     UE8M0 scales as uint8_t.  All arrays are dense and row-major.
+ *   - FP4 packing: element 2i of a row in the low nibble of byte i, element
+ *     2i+1 in the high nibble.  Scales: one byte per 32 consecutive elements
+ *     of a row, value 2^(b - 127).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)        /* bad pointer, size or shape */
+#define MOE_EUNSUPPORTED (-2)  /* shape outside what the kernels handle */
+#define MOE_EWORKSPACE (-3)    /* workspace too small or misaligned */
+#define MOE_EHIP (-4)          /* HIP runtime / launch failure */
+
+#define MOE_SCORE_SOFTMAX 0
+#define MOE_SCORE_SIGMOID 1
+
+/* Layer shape.
+ *   T         tokens (>= 0; T == 0 is a no-op)
+ *   H         hidden size, multiple of 128
+ *   I         intermediate size of one projection (gate or up), multiple of 128
+ *   E         experts, 1..1024
+ *   topk      experts per token, 1..min(E, 16)
+ *   score_fn  MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID (routing inside the library)
+ *   renorm    nonzero: the k weights are divided by their sum */
+typedef struct moe_dims {
+    int64_t T;
+    int32_t H;
+    int32_t I;
+    int32_t E;
+    int32_t topk;
+    int32_t score_fn;
+    int32_t renorm;
+} moe_dims_t;
+
+/* Flags of moe_forward. */
+#define MOE_FLAG_NONE 0u
+
+#define MOE_NUM_STAGE_EVENTS 5
+
+/* Arguments of moe_forward.
+ *   x         device, BF16 [T, H]
+ *   logits    device, float32 [T, E] router logits; or NULL, and then
+ *   topk_idx  device, int32 [T, topk] expert ids (entries < 0 are skipped) and
+ *   topk_w    device, float32 [T, topk] routing weights
+ *   w13       device, FP4 [E, 2I, H/2]: rows [0, I) gate (W1), [I, 2I) up (W3)
+ *   w13_sf    device, UE8M0 [E, 2I, H/32]
+ *   w2        device, FP4 [E, H, I/2]
+ *   w2_sf     device, UE8M0 [E, H, I/32]
+ *   y         device, BF16 [T, H], written
+ *   ws        device workspace of at least moe_workspace_size() bytes,
+ *             256-byte aligned, zeroed once by moe_workspace_init() after it is
+ *             allocated; every call leaves it ready for the next call.  One
+ *             workspace must not be used by two calls that may overlap.
+ *   stage_events  NULL, or MOE_NUM_STAGE_EVENTS caller-created HIP events that
+ *             are recorded on s before routing, before GEMM1, before GEMM2,
+ *             before the combine and after it (for per-stage timing). */
+typedef struct moe_args {
+    moe_dims_t dims;
+    const uint16_t* x;
+    const float* logits;
+    const int32_t* topk_idx;
+    const float* topk_w;
+    const uint8_t* w13;
+    const uint8_t* w13_sf;
+    const uint8_t* w2;
+    const uint8_t* w2_sf;
+    uint16_t* y;
+    void* ws;
+    size_t ws_bytes;
+    uint32_t flags;
+    hipEvent_t* stage_events;
+} moe_args_t;
+
+/* Byte offsets of the intermediates inside the workspace after moe_forward
+ * (for inspection and tests).  Positions p are slot positions: expert e owns
+ * p in [offsets[e], offsets[e+1]).
+ *   topk_idx  int32 [T, topk]     routing result used (copy of the input ids
+ *                                 when the caller routed)
+ *   topk_w    float32 [T, topk]
+ *   counts    int32 [E]
+ *   offsets   int32 [E + 1]       exclusive prefix sum of counts
+ *   slot_src  int32 [T*topk]      t*topk + j of position p (first offsets[E] valid)
+ *   slot_of   int32 [T, topk]     position of pair (t, j), -1 when skipped
+ *   xq, xsf   uint8 [T, H], [T, H/32]            quantised x
+ *   hq, hsf   uint8 [T*topk, I], [T*topk, I/32]  quantised h by position
+ *   o         BF16 [T*topk, H]                  GEMM2 rows by position */
+typedef struct moe_layout {
+    size_t topk_idx, topk_w, counts, offsets, slot_src, slot_of;
+    size_t xq, xsf, hq, hsf, o;
+    size_t total;
+} moe_layout_t;
+
+/* Size in bytes of the workspace moe_forward and moe_route need for d. */
+int moe_workspace_size(const moe_dims_t* d, size_t* bytes);
+
+/* Offsets of the intermediates in the workspace for d. */
+int moe_workspace_layout(const moe_dims_t* d, moe_layout_t* out);
+
+/* Zero a freshly allocated workspace (enqueued on s).  Needed once per
+ * allocation: the library's internal counters must start at zero, and each
+ * call resets them before it returns ("MonoMoe kernel — design" §4 keys the
+ * same one-time zeroing on the buffer's identity). */
+int moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Top-k routing and counting-sort bucketisation ("MonoMoe kernel — design" §1
+ * phase 1; "05.10 Counting Sort / Bucketization" sections 2.1-2.3).
+ *   logits    device float32 [T, E]
+ *   topk_idx  device int32 [T, topk] out: chosen experts, decreasing logit,
+ *             equal logits by increasing expert id
+ *   topk_w    device float32 [T, topk] out: weights (see moe_dims_t)
+ *   counts    device int32 [E] out
+ *   offsets   device int32 [E + 1] out: exclusive prefix sum of counts
+ *   slot_src  device int32 [T*topk] out: t*topk + j for each position; the
+ *             order inside an expert's segment is unspecified
+ *   slot_of   device int32 [T, topk] out: position of (t, j)
+ *   ws        workspace as for moe_forward */
+int moe_route(const moe_dims_t* d, const float* logits, int32_t* topk_idx, float* topk_w,
+              int32_t* counts, int32_t* offsets, int32_t* slot_src, int32_t* slot_of,
+              void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Per-row activation quantisation ("MegaMoE" notes, "Dispatch阶段"): each group
+ * of 32 consecutive elements of a row gets the smallest power-of-two scale s
+ * with max|v| <= 448 s, and codes v/s rounded to nearest-even E4M3.
+ *   x   device BF16 [rows, cols]; cols a multiple of 32
+ *   q   device uint8 [rows, cols] out: E4M3 codes
+ *   sf  device uint8 [rows, cols/32] out: UE8M0 scale bytes */
+int moe_quant_act(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* q, uint8_t* sf,
+                  hipStream_t s);
+
+/* Weight quantisation ("MegaMoE" notes, "Expert矩阵权重量化"): BF16 [rows, cols]
+ * to FP4 E2M1 with one UE8M0 scale per 32 consecutive elements of a row
+ * (smallest power of two s with max|v| <= 6 s; nearest-even codes).
+ *   w   device BF16 [rows, cols]; cols a multiple of 32
+ *   q   device uint8 [rows, cols/2] out: packed E2M1
+ *   sf  device uint8 [rows, cols/32] out */
+int moe_pack_weights(const uint16_t* w, int64_t rows, int32_t cols, uint8_t* q, uint8_t* sf,
+                     hipStream_t s);
+
+/* The whole layer: route (or take topk_idx/topk_w), bucketise, quantise x,
+ * GEMM1 + SwiGLU*weight -> FP8, GEMM2 -> BF16, combine into y. */
+int moe_forward(const moe_args_t* a, hipStream_t s);
+
+/* Static text for a return code (for MOE_EHIP: the calling thread's last HIP
+ * error message). */
+const char* moe_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,269 @@
+// Host side of the C ABI declared in include/moe.h: argument checks, the
+// workspace carve, and the launch sequence of the layer.
+#include <string>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_hip_error;
+
+int hip_fail(hipError_t err) {
+    g_hip_error = hipGetErrorString(err);
+    return MOE_EHIP;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Carve {
+    size_t cnt, arrive, counts, offsets, mtile_off, mtile_e, topk_idx, topk_w, slot_in_e, slot_src, slot_of;
+    size_t xq, xsf, hq, hsf, o, total;
+};
+
+Carve carve(const moe_dims_t& d) {
+    Carve c{};
+    const size_t T = (size_t)d.T, E = (size_t)d.E, k = (size_t)d.topk, R = T * k;
+    size_t at = 0;
+    auto take = [&](size_t bytes) { size_t off = at; at = align_up(at + bytes); return off; };
+    c.cnt = take(E * 4);
+    c.arrive = take(64);
+    c.counts = take(E * 4);
+    c.offsets = take((E + 1) * 4);
+    c.mtile_off = take((E + 1) * 4);
+    c.mtile_e = take(((R + moe::gemm_bm() - 1) / moe::gemm_bm() + std::min(E, R) + 1) * 4);
+    c.topk_idx = take(R * 4);
+    c.topk_w = take(R * 4);
+    c.slot_in_e = take(R * 4);
+    c.slot_src = take(R * 4);
+    c.slot_of = take(R * 4);
+    c.xq = take(T * (size_t)d.H);
+    c.xsf = take(T * (size_t)d.H / 32);
+    c.hq = take(R * (size_t)d.I);
+    c.hsf = take(R * (size_t)d.I / 32);
+    c.o = take(R * (size_t)d.H * 2);
+    c.total = at;
+    return c;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+int check_dims(const moe_dims_t* d) {
+    if (!d) return MOE_EINVAL;
+    if (d->T < 0 || d->T > (1ll << 24)) return MOE_EINVAL;
+    if (d->H <= 0 || d->I <= 0 || d->E <= 0 || d->topk <= 0) return MOE_EINVAL;
+    if (d->topk > d->E || d->topk > 16 || d->E > 1024) return MOE_EUNSUPPORTED;
+    if (d->H % 128 != 0 || d->I % 128 != 0) return MOE_EUNSUPPORTED;
+    if (d->score_fn != MOE_SCORE_SOFTMAX && d->score_fn != MOE_SCORE_SIGMOID) return MOE_EINVAL;
+    if ((int64_t)d->T * d->topk * (int64_t)d->H >= (1ll << 40)) return MOE_EUNSUPPORTED;
+    return MOE_OK;
+}
+
+__global__ void zero_kernel(uint4* p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0, 0, 0, 0);
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off); }
+
+}  // namespace
+
+extern "C" {
+
+int moe_workspace_size(const moe_dims_t* d, size_t* bytes) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if (!bytes) return MOE_EINVAL;
+    *bytes = carve(*d).total;
+    return MOE_OK;
+}
+
+int moe_workspace_layout(const moe_dims_t* d, moe_layout_t* out) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if (!out) return MOE_EINVAL;
+    Carve c = carve(*d);
+    out->topk_idx = c.topk_idx;
+    out->topk_w = c.topk_w;
+    out->counts = c.counts;
+    out->offsets = c.offsets;
+    out->slot_src = c.slot_src;
+    out->slot_of = c.slot_of;
+    out->xq = c.xq;
+    out->xsf = c.xsf;
+    out->hq = c.hq;
+    out->hsf = c.hsf;
+    out->o = c.o;
+    out->total = c.total;
+    return MOE_OK;
+}
+
+int moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t s) {
+    if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes % 16 != 0) return MOE_EINVAL;
+    size_t n16 = ws_bytes / 16;
+    if (n16 == 0) return MOE_OK;
+    unsigned grid = (unsigned)std::min<size_t>((n16 + 255) / 256, 4096);
+    hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, static_cast<uint4*>(ws), n16);
+    hipError_t err = hipGetLastError();
+    return err == hipSuccess ? MOE_OK : hip_fail(err);
+}
+
+int moe_route(const moe_dims_t* d, const float* logits, int32_t* topk_idx, float* topk_w,
+              int32_t* counts, int32_t* offsets, int32_t* slot_src, int32_t* slot_of, void* ws,
+              size_t ws_bytes, hipStream_t s) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if (!logits || !topk_idx || !topk_w || !counts || !offsets || !slot_src || !slot_of || !ws)
+        return MOE_EINVAL;
+    Carve c = carve(*d);
+    if (ws_bytes < c.total || ((uintptr_t)ws % kAlign) != 0) return MOE_EWORKSPACE;
+    moe::RouteParams rp{};
+    rp.logits = logits;
+    rp.idx_out = topk_idx;
+    rp.w_out = topk_w;
+    rp.cnt = at<int>(ws, c.cnt);
+    rp.slot_in_e = at<int32_t>(ws, c.slot_in_e);
+    rp.T = d->T;
+    rp.H = d->H;
+    rp.E = d->E;
+    rp.topk = d->topk;
+    rp.score_fn = d->score_fn;
+    rp.renorm = d->renorm;
+    moe::ScatterParams sp{};
+    sp.idx = topk_idx;
+    sp.slot_in_e = rp.slot_in_e;
+    sp.cnt = rp.cnt;
+    sp.arrive = at<unsigned>(ws, c.arrive);
+    sp.counts_out = counts;
+    sp.offsets_out = offsets;
+    sp.mtile_off = at<int32_t>(ws, c.mtile_off);
+    sp.mtile_e = at<int32_t>(ws, c.mtile_e);
+    sp.slot_src = slot_src;
+    sp.slot_of = slot_of;
+    sp.T = d->T;
+    sp.E = d->E;
+    sp.topk = d->topk;
+    sp.bm = moe::gemm_bm();
+    hipError_t err = moe::launch_route(rp, sp, s);
+    return err == hipSuccess ? MOE_OK : hip_fail(err);
+}
+
+int moe_quant_act(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* q, uint8_t* sf,
+                  hipStream_t s) {
+    if (rows < 0 || cols <= 0 || cols % 32 != 0) return MOE_EINVAL;
+    if (rows == 0) return MOE_OK;
+    if (!x || !q || !sf || !aligned16(x) || ((uintptr_t)q & 7) != 0) return MOE_EINVAL;
+    hipError_t err = moe::launch_quant_act(x, rows, cols, q, sf, s);
+    return err == hipSuccess ? MOE_OK : hip_fail(err);
+}
+
+int moe_pack_weights(const uint16_t* w, int64_t rows, int32_t cols, uint8_t* q, uint8_t* sf,
+                     hipStream_t s) {
+    if (rows < 0 || cols <= 0 || cols % 32 != 0) return MOE_EINVAL;
+    if (rows == 0) return MOE_OK;
+    if (!w || !q || !sf || !aligned16(w) || ((uintptr_t)q & 3) != 0) return MOE_EINVAL;
+    hipError_t err = moe::launch_pack_weights(w, rows, cols, q, sf, s);
+    return err == hipSuccess ? MOE_OK : hip_fail(err);
+}
+
+int moe_forward(const moe_args_t* a, hipStream_t s) {
+    if (!a) return MOE_EINVAL;
+    const moe_dims_t& d = a->dims;
+    int rc = check_dims(&d);
+    if (rc) return rc;
+    if (d.T == 0) return MOE_OK;
+    if (!a->x || !a->w13 || !a->w13_sf || !a->w2 || !a->w2_sf || !a->y || !a->ws) return MOE_EINVAL;
+    if (!a->logits && (!a->topk_idx || !a->topk_w)) return MOE_EINVAL;
+    if (!aligned16(a->x) || !aligned16(a->w13) || !aligned16(a->w2) || !aligned16(a->y) ||
+        ((uintptr_t)a->w13_sf & 3) || ((uintptr_t)a->w2_sf & 3))
+        return MOE_EINVAL;
+    Carve c = carve(d);
+    if (a->ws_bytes < c.total || ((uintptr_t)a->ws % kAlign) != 0) return MOE_EWORKSPACE;
+    void* ws = a->ws;
+
+    moe::RouteParams rp{};
+    rp.logits = a->logits;
+    rp.idx_in = a->topk_idx;
+    rp.w_in = a->topk_w;
+    rp.idx_out = at<int32_t>(ws, c.topk_idx);
+    rp.w_out = at<float>(ws, c.topk_w);
+    rp.cnt = at<int>(ws, c.cnt);
+    rp.slot_in_e = at<int32_t>(ws, c.slot_in_e);
+    rp.x = a->x;
+    rp.xq = at<uint8_t>(ws, c.xq);
+    rp.xsf = at<uint8_t>(ws, c.xsf);
+    rp.T = d.T;
+    rp.H = d.H;
+    rp.E = d.E;
+    rp.topk = d.topk;
+    rp.score_fn = d.score_fn;
+    rp.renorm = d.renorm;
+    moe::ScatterParams sp{};
+    sp.idx = rp.idx_out;
+    sp.slot_in_e = rp.slot_in_e;
+    sp.cnt = rp.cnt;
+    sp.arrive = at<unsigned>(ws, c.arrive);
+    sp.counts_out = at<int32_t>(ws, c.counts);
+    sp.offsets_out = at<int32_t>(ws, c.offsets);
+    sp.mtile_off = at<int32_t>(ws, c.mtile_off);
+    sp.mtile_e = at<int32_t>(ws, c.mtile_e);
+    sp.slot_src = at<int32_t>(ws, c.slot_src);
+    sp.slot_of = at<int32_t>(ws, c.slot_of);
+    sp.T = d.T;
+    sp.E = d.E;
+    sp.topk = d.topk;
+    sp.bm = moe::gemm_bm();
+    hipEvent_t* ev = a->stage_events;
+    hipError_t err = ev ? hipEventRecord(ev[0], s) : hipSuccess;
+    if (err == hipSuccess) err = moe::launch_route(rp, sp, s);
+    if (err != hipSuccess) return hip_fail(err);
+
+    moe::GemmParams gp{};
+    gp.offsets = sp.offsets_out;
+    gp.mtile_off = sp.mtile_off;
+    gp.mtile_e = sp.mtile_e;
+    gp.slot_src = sp.slot_src;
+    gp.topk_w = rp.w_out;
+    gp.xq = rp.xq;
+    gp.xsf = rp.xsf;
+    gp.w13 = a->w13;
+    gp.w13sf = a->w13_sf;
+    gp.hq = at<uint8_t>(ws, c.hq);
+    gp.hsf = at<uint8_t>(ws, c.hsf);
+    gp.w2 = a->w2;
+    gp.w2sf = a->w2_sf;
+    gp.o = at<uint16_t>(ws, c.o);
+    gp.T = d.T;
+    gp.H = d.H;
+    gp.I = d.I;
+    gp.E = d.E;
+    gp.topk = d.topk;
+    const int64_t R = d.T * d.topk;
+    const int bm = moe::gemm_bm();
+    gp.max_mtiles = (int)((R + bm - 1) / bm + std::min<int64_t>(d.E, R));
+    if (ev) err = hipEventRecord(ev[1], s);
+    if (err == hipSuccess) err = moe::launch_gemm1(gp, s);
+    if (err == hipSuccess && ev) err = hipEventRecord(ev[2], s);
+    if (err == hipSuccess) err = moe::launch_gemm2(gp, s);
+    if (err == hipSuccess && ev) err = hipEventRecord(ev[3], s);
+    if (err == hipSuccess) err = moe::launch_combine(gp.o, sp.slot_of, d.T, d.topk, d.H, a->y, s);
+    if (err == hipSuccess && ev) err = hipEventRecord(ev[4], s);
+    return err == hipSuccess ? MOE_OK : hip_fail(err);
+}
+
+const char* moe_error_string(int code) {
+    switch (code) {
+        case MOE_OK: return "success";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_EUNSUPPORTED: return "unsupported shape";
+        case MOE_EWORKSPACE: return "workspace too small or misaligned";
+        case MOE_EHIP: return g_hip_error.empty() ? "HIP error" : g_hip_error.c_str();
+        default: return "unknown error";
+    }
+}
+
+}  // extern "C"

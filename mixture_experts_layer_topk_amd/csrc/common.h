@@ -1,0 +1,108 @@
+// Device primitives shared by the layer's kernels (gfx950).
+//
+// Number formats (pages: "MegaMoE" study notes, "Dispatch阶段" and
+// "Expert矩阵权重量化"; read as OCP MX v1.0):
+//   E4M3 ("FN"): bias 7, largest finite 448, no infinities, subnormals m*2^-9
+//   E2M1:        magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}
+//   UE8M0:       2^(b - 127)
+// A group of 32 values shares the smallest power-of-two scale 2^e with
+// max|v| <= Q * 2^e (Q = 448 or 6); codes are v * 2^-e rounded to the nearest
+// representable value, ties to the even code, sign kept.  The exponent is read
+// off the float32 bit fields of max|v|: with max|v| = m * 2^E, m in [1, 2),
+// e = E - 8 + [m > 1.75] for E4M3 and e = E - 2 + [m > 1.5] for E2M1.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+#define MOE_DEV static __device__ __forceinline__
+
+namespace moe {
+
+constexpr int kGroup = 32;          // elements per UE8M0 scale
+constexpr int kFmtFp8 = 0;          // scaled-MFMA format selector: FP8 E4M3
+constexpr int kFmtFp4 = 4;          // scaled-MFMA format selector: FP4 E2M1
+
+MOE_DEV uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+MOE_DEV float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+MOE_DEV float bf16_to_f32(uint32_t b) { return u2f(b << 16); }
+
+// float32 -> BF16, nearest even (inputs are finite).
+MOE_DEV uint32_t f32_to_bf16(float f) {
+    uint32_t u = f2u(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Block exponent e (clamped to [-127, 127]) for a group whose largest
+// magnitude is amax (finite, >= 0).  kMantThresh is the mantissa field of
+// Q's significand: 0x600000 (1.75, E4M3) or 0x400000 (1.5, E2M1); kShift is
+// log2 of Q's binade (8 for 448, 2 for 6).
+template <uint32_t kMantThresh, int kShift>
+MOE_DEV int block_exp(float amax) {
+    uint32_t a = f2u(amax) & 0x7FFFFFFFu;
+    if (a == 0) return 0;
+    int E = (int)(a >> 23) - 127;
+    if ((a >> 23) == 0) return -127;               // float32 subnormal: below E8M0 range
+    int e = E - kShift + ((a & 0x7FFFFFu) > kMantThresh ? 1 : 0);
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+MOE_DEV int e4m3_block_exp(float amax) { return block_exp<0x600000u, 8>(amax); }
+MOE_DEV int e2m1_block_exp(float amax) { return block_exp<0x400000u, 2>(amax); }
+
+// 2^-e as a float for e in [-127, 127] (2^-127 is a float32 subnormal).
+MOE_DEV float exp2_neg(int e) { return __builtin_ldexpf(1.0f, -e); }
+
+// |x| <= 448 expected; larger magnitudes clamp to 448.  Nearest even.
+MOE_DEV uint32_t e4m3_encode(float x) {
+    uint32_t u = f2u(x);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t mag;
+    if (a >= 0x43E00000u) {                          // >= 448
+        mag = 0x7Eu;
+    } else if (a < 0x3C800000u) {                    // < 2^-6: subnormal grid m * 2^-9
+        mag = (uint32_t)__builtin_rintf(u2f(a) * 512.0f);   // exact scaling, RNE; 8 -> 2^-6
+    } else {
+        // rebias exponent 127 -> 7 and drop 20 mantissa bits, nearest even
+        uint32_t r = a - (120u << 23);
+        uint32_t q = r >> 20;
+        uint32_t rem = r & 0xFFFFFu;
+        q += (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u;
+        mag = q;
+    }
+    return sign | mag;
+}
+
+// |x| <= 6 expected; larger magnitudes clamp to 6.  Nearest, ties to the even
+// code: the code is the number of decision thresholds below |x|, a threshold
+// being the midpoint between neighbouring magnitudes, counted at equality when
+// the upper neighbour has the even code.
+MOE_DEV uint32_t e2m1_encode(float x) {
+    uint32_t sign = (f2u(x) >> 28) & 0x8u;
+    float a = __builtin_fabsf(x);
+    uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
+                 (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+    return sign | c;
+}
+
+MOE_DEV int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Wave-level reductions over 64 lanes.
+MOE_DEV float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+MOE_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,381 @@
+// Grouped block-scaled GEMMs of the expert MLP on gfx950 matrix cores.
+//
+// GEMM1 ("MegaMoE" notes, "GEMM" and the flow chart; "MegaMoE：把通信和计算融合
+// 到一个 Mega Kernel", "L1/L2 交错" table): for every expert e and every position
+// p of its segment, acc[n] = sum_K dq(xq[token(p)]) * dq(W13[e, n]) with FP8
+// activations and FP4 weights, one UE8M0 scale per 32 K on both sides, FP32
+// accumulation.  Epilogue ("L1 epilogue"; "Warp Specialization" L1 epilogue
+// excerpt): h = silu(gate) * up * topk_weight on the FP32 accumulators, then
+// per 32 columns of I the smallest power-of-two scale and E4M3 codes.
+// GEMM2 ("L2 epilogue"): out[p, n] = sum_I dq(hq[p]) * dq(W2[e, n]) in FP32,
+// rounded to BF16.
+//
+// Mapping to the hardware.  One V_MFMA_SCALE_F32_16X16X128_F8F6F4 multiplies a
+// 16 x 128 FP8 tile by a 128 x 16 FP4 tile and applies the E8M0 scales itself.
+// With g = l / 16, lane l supplies (layout measured on gfx950):
+//   A (FP8): row l % 16, K [16 g, 16 g + 16) in bytes 0-15 and
+//            K [64 + 16 g, 64 + 16 g + 16) in bytes 16-31;
+//   B (FP4): column l % 16, K [32 g, 32 g + 32) in bytes 0-15;
+//   scales:  the E8M0 byte of row (column) l % 16 for K group [32 g, 32 g + 32);
+// and receives rows 4 g + i, column l % 16 of the 16 x 16 FP32 result.
+//
+// A workgroup owns a BM x BN output tile and loops over K in steps of 128.
+// The waves form a WM x WN grid; each wave computes (BM/WM) x (BN/WN) with
+// MT x NT MFMA tiles.
+//
+// Column permutation.  The B tile's LDS row order is chosen so that a lane's
+// NT accumulator columns are contiguous output columns: within a wave's slice,
+// LDS row nt*16 + c holds output column c*NT + nt.  For GEMM1 the slice's
+// MFMA column tiles alternate gate (even nt) and up (odd nt) for the same
+// I columns, so SwiGLU pairs acc[2q] with acc[2q+1] inside one lane and a lane
+// owns NT/2 consecutive h columns; an E4M3 group of 32 columns is then
+// 32/(NT/2) neighbouring lanes.  The canonical weight layout (gate rows, then
+// up rows) is read as is; the pages' offline 8-row gate/up interleave
+// ("原始权重布局") is replaced by this in-loader permutation.
+//
+// Tiles are handed out persistently: workgroup b takes tiles b, b + grid, ...
+// in (m-tile, n-tile) order, n fastest; an m-tile is BM consecutive positions
+// of one expert (the last one ragged), looked up in the per-m-tile expert
+// table the bucketisation writes.
+//
+// Loads go straight from global memory to LDS (global_load_lds_dwordx4): one
+// instruction fills 1 KiB of LDS contiguously, lane l landing at byte 16 l, so
+// the XOR swizzle of the LDS tiles is applied on the global side by choosing
+// which 16-byte chunk each lane fetches.  Three LDS stages are in flight: the
+// loads of step ks + 2 are issued while step ks is multiplied.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int BK = 128;                 // K per MFMA step (bytes of FP8 A per row)
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int BM, int BN, int WM, int WN, bool kG1>
+struct Cfg {
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int WTM = BM / WM;             // wave tile rows
+    static constexpr int WTN = BN / WN;             // wave tile cols
+    static constexpr int MT = WTM / 16;
+    static constexpr int NT = WTN / 16;
+    static constexpr int kABytes = BM * BK;         // FP8
+    static constexpr int kBBytes = BN * BK / 2;     // FP4
+    static constexpr int kSABytes = BM * 4;
+    static constexpr int kSBBytes = BN * 4;
+    static constexpr int kStage = kABytes + kBBytes + kSABytes + kSBBytes;
+    static constexpr int kStages = 3;
+    static constexpr int kAI = kABytes / 1024 / kWaves;   // 1 KiB load instructions per wave
+    static constexpr int kBI = kBBytes / 1024 / kWaves;
+    static constexpr int kSAI = kSABytes / 256 / kWaves;  // 256-byte (dword per lane) loads
+    static constexpr int kSBI = kSBBytes / 256 / kWaves;
+    static constexpr int kLoads = kAI + kBI + kSAI + kSBI;  // per thread per stage
+    static_assert(kABytes % (1024 * kWaves) == 0 && kBBytes % (1024 * kWaves) == 0, "tile / waves");
+    static_assert(kSABytes % (256 * kWaves) == 0 && kSBBytes % (256 * kWaves) == 0, "scales / waves");
+    static_assert(MT >= 1 && NT >= 2 && NT % 2 == 0, "wave tile");
+    static_assert(kLoads < 64, "vmcnt range");
+};
+
+// A: row r, 16-byte chunk c (of 8) -> swizzled byte offset inside the A tile.
+MOE_DEV int a_off(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 4); }
+// B: row n, 16-byte chunk c (of 4) -> swizzled byte offset inside the B tile.
+MOE_DEV int b_off(int n, int c) { return n * (BK / 2) + ((c ^ ((n >> 2) & 3)) << 4); }
+
+MOE_DEV v4f mfma_fp8_fp4(const v8i& a, const v4i& b, const v4f& c, int sa, int sb) {
+    v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b8, c, kFmtFp8, kFmtFp4, 0, sa, 0,
+                                                            sb);
+}
+
+MOE_DEV float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] in bits [15:14]).
+template <int N>
+MOE_DEV void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence: LDS traffic is ordered by the
+// explicit vmcnt waits around it; the empty asm keeps the compiler from moving
+// memory operations across it.
+MOE_DEV void barrier_nofence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+MOE_DEV void load_lds16(const void* g, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
+}
+MOE_DEV void load_lds4(const void* g, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 4, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, bool kG1>
+__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParams p) {
+    using C = Cfg<BM, BN, WM, WN, kG1>;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    int* s_tok = reinterpret_cast<int*>(smem + C::kStages * C::kStage);   // [BM] A row source
+    float* s_w = reinterpret_cast<float*>(s_tok + BM);                     // [BM] topk weight
+    __shared__ int s_tile[4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int l16 = lane & 15, lg = lane >> 4;
+
+    const int K = kG1 ? p.H : p.I;                 // reduction length
+    const int nk = K / BK;
+    const int NTILES = kG1 ? (2 * p.I) / BN : (p.H + BN - 1) / BN;
+    const int sf_stride = K / kGroup;              // scale bytes per row
+    const uint8_t* a_base = kG1 ? p.xq : p.hq;
+    const uint8_t* sa_base = kG1 ? p.xsf : p.hsf;
+
+    if (tid == 0) s_tile[3] = p.mtile_off[p.E];
+    __syncthreads();
+    const int total = s_tile[3] * NTILES;
+
+    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+        const int mt_g = tile / NTILES;
+        const int ntile = tile - mt_g * NTILES;
+        if (tid == 0) {
+            const int e = p.mtile_e[mt_g];
+            s_tile[0] = e;
+            s_tile[1] = p.offsets[e] + (mt_g - p.mtile_off[e]) * BM;
+            s_tile[2] = p.offsets[e + 1];
+        }
+        __syncthreads();
+        const int e = s_tile[0];
+        const int p0 = s_tile[1];
+        const int valid = min(BM, s_tile[2] - p0);
+
+        // row sources of the A tile: token rows (GEMM1) or positions (GEMM2)
+        if (tid < BM) {
+            int pr = p0 + min(tid, valid - 1);
+            if (kG1) {
+                int src = p.slot_src[pr];
+                s_tok[tid] = src / p.topk;
+                s_w[tid] = p.topk_w[src];
+            } else {
+                s_tok[tid] = pr;
+            }
+        }
+        __syncthreads();
+
+        // B tile LDS row -> weight row.  Inside a wave's slice, LDS row nt*16 + c
+        // holds output column c*NT + nt (GEMM2) or, for GEMM1, I column
+        // c*NT/2 + nt/2 of the gate (even nt) or up (odd nt) projection.
+        auto b_row = [&](int b) -> int {
+            int ws = b / C::WTN, bl = b % C::WTN;
+            int nt = bl >> 4, c = bl & 15;
+            if (kG1) {
+                int icol = ntile * (BN / 2) + ws * (C::WTN / 2) + c * (C::NT / 2) + (nt >> 1);
+                return (nt & 1) ? p.I + icol : icol;
+            } else {
+                int n = ntile * BN + ws * C::WTN + c * C::NT + nt;
+                return min(n, p.H - 1);
+            }
+        };
+        const int64_t b_stride = K / 2;
+        const uint8_t* w_base = kG1 ? p.w13 + (int64_t)e * (2 * p.I) * b_stride
+                                    : p.w2 + (int64_t)e * p.H * b_stride;
+        const uint8_t* wsf_base = kG1 ? p.w13sf + (int64_t)e * (2 * p.I) * sf_stride
+                                      : p.w2sf + (int64_t)e * p.H * sf_stride;
+
+        // per-lane global sources of each load instruction (fixed over K)
+        const uint8_t* a_src[C::kAI];
+#pragma unroll
+        for (int j = 0; j < C::kAI; ++j) {
+            int r = 8 * (j * C::kWaves + wave) + (lane >> 3);
+            int c = (lane & 7) ^ ((r >> 1) & 7);
+            a_src[j] = a_base + (int64_t)s_tok[r] * K + c * 16;
+        }
+        const uint8_t* b_src[C::kBI];
+#pragma unroll
+        for (int j = 0; j < C::kBI; ++j) {
+            int n = 16 * (j * C::kWaves + wave) + (lane >> 2);
+            int c = (lane & 3) ^ ((n >> 2) & 3);
+            b_src[j] = w_base + (int64_t)b_row(n) * b_stride + c * 16;
+        }
+        const uint8_t* sa_src[C::kSAI];
+#pragma unroll
+        for (int j = 0; j < C::kSAI; ++j) {
+            int r = 64 * (j * C::kWaves + wave) + lane;
+            sa_src[j] = sa_base + (int64_t)s_tok[r] * sf_stride;
+        }
+        const uint8_t* sb_src[C::kSBI];
+#pragma unroll
+        for (int j = 0; j < C::kSBI; ++j) {
+            int n = 64 * (j * C::kWaves + wave) + lane;
+            sb_src[j] = wsf_base + (int64_t)b_row(n) * sf_stride;
+        }
+
+        auto issue = [&](int ks) {
+            uint8_t* sA = smem + (ks % C::kStages) * C::kStage;
+            uint8_t* sB = sA + C::kABytes;
+            uint8_t* sSA = sB + C::kBBytes;
+            uint8_t* sSB = sSA + C::kSABytes;
+            const int ka = ks * BK, kb = ks * (BK / 2), kg = ks * (BK / kGroup);
+#pragma unroll
+            for (int j = 0; j < C::kAI; ++j)
+                load_lds16(a_src[j] + ka, sA + (j * C::kWaves + wave) * 1024);
+#pragma unroll
+            for (int j = 0; j < C::kBI; ++j)
+                load_lds16(b_src[j] + kb, sB + (j * C::kWaves + wave) * 1024);
+#pragma unroll
+            for (int j = 0; j < C::kSAI; ++j)
+                load_lds4(sa_src[j] + kg, sSA + (j * C::kWaves + wave) * 256);
+#pragma unroll
+            for (int j = 0; j < C::kSBI; ++j)
+                load_lds4(sb_src[j] + kg, sSB + (j * C::kWaves + wave) * 256);
+        };
+
+        v4f acc[C::MT][C::NT];
+#pragma unroll
+        for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NT; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+        wait_vmcnt<0>();
+        issue(0);
+        if (nk > 1) issue(1);
+        for (int ks = 0; ks < nk; ++ks) {
+            // stage ks landed (the loads of ks + 1 may still be in flight)
+            if (ks + 1 < nk) wait_vmcnt<C::kLoads>(); else wait_vmcnt<0>();
+            barrier_nofence();          // every lane's stage-ks data; stage (ks+2)%3 no longer read
+            if (ks + 2 < nk) issue(ks + 2);
+            const uint8_t* sA = smem + (ks % C::kStages) * C::kStage;
+            const uint8_t* sB = sA + C::kABytes;
+            const uint8_t* sSA = sB + C::kBBytes;
+            const uint8_t* sSB = sSA + C::kSABytes;
+            v4i bf[C::NT];
+            int sbv[C::NT];
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt) {
+                int n = wn * C::WTN + nt * 16 + l16;
+                bf[nt] = *reinterpret_cast<const v4i*>(sB + b_off(n, lg));
+                sbv[nt] = sSB[n * 4 + lg];
+            }
+#pragma unroll
+            for (int mt = 0; mt < C::MT; ++mt) {
+                int r = wm * C::WTM + mt * 16 + l16;
+                v4i lo = *reinterpret_cast<const v4i*>(sA + a_off(r, lg));
+                v4i hi = *reinterpret_cast<const v4i*>(sA + a_off(r, 4 + lg));
+                v8i af = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                int sav = sSA[r * 4 + lg];
+#pragma unroll
+                for (int nt = 0; nt < C::NT; ++nt)
+                    acc[mt][nt] = mfma_fp8_fp4(af, bf[nt], acc[mt][nt], sav, sbv[nt]);
+            }
+        }
+
+        // ---------------------------------------------------------------- epilogue
+        if (kG1) {
+            // lane holds, for row 4*lg + i of m-tile mt, the h columns
+            // icol0 + l16*(NT/2) + q, q < NT/2 (gate acc[2q], up acc[2q+1])
+            constexpr int QN = C::NT / 2;
+            const int icol0 = ntile * (BN / 2) + wn * (C::WTN / 2);
+#pragma unroll
+            for (int mt = 0; mt < C::MT; ++mt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = wm * C::WTM + mt * 16 + 4 * lg + i;
+                    const float wr = s_w[r];
+                    float h[QN];
+                    float amax = 0.f;
+#pragma unroll
+                    for (int q = 0; q < QN; ++q) {
+                        float g = acc[mt][2 * q][i], u = acc[mt][2 * q + 1][i];
+                        h[q] = silu(g) * u * wr;
+                        amax = fmaxf(amax, __builtin_fabsf(h[q]));
+                    }
+                    // a 32-column group spans 32 / QN neighbouring lanes of the 16
+#pragma unroll
+                    for (int o = 1; o < 32 / QN; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+                    const int ex = e4m3_block_exp(amax);
+                    const float inv = exp2_neg(ex);
+                    if (r < valid) {
+                        const int64_t pos = p0 + r;
+                        const int col = icol0 + l16 * QN;
+                        uint8_t* dst = p.hq + pos * p.I + col;
+                        if constexpr (QN == 4) {
+                            uint32_t v = 0;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) v |= e4m3_encode(h[q] * inv) << (8 * q);
+                            *reinterpret_cast<uint32_t*>(dst) = v;
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < QN; ++q) dst[q] = (uint8_t)e4m3_encode(h[q] * inv);
+                        }
+                        if ((col & (kGroup - 1)) == 0)
+                            p.hsf[pos * (p.I / kGroup) + col / kGroup] = (uint8_t)(ex + 127);
+                    }
+                }
+            }
+        } else {
+            // lane holds row 4*lg + i, output columns n0 + l16*NT + nt, nt < NT
+            const int n0 = ntile * BN + wn * C::WTN + l16 * C::NT;
+#pragma unroll
+            for (int mt = 0; mt < C::MT; ++mt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = wm * C::WTM + mt * 16 + 4 * lg + i;
+                    if (r < valid && n0 < p.H) {
+                        uint16_t* dst = p.o + (int64_t)(p0 + r) * p.H + n0;
+                        if constexpr (C::NT == 8) {
+                            uint4 v;
+                            v.x = f32_to_bf16(acc[mt][0][i]) | (f32_to_bf16(acc[mt][1][i]) << 16);
+                            v.y = f32_to_bf16(acc[mt][2][i]) | (f32_to_bf16(acc[mt][3][i]) << 16);
+                            v.z = f32_to_bf16(acc[mt][4][i]) | (f32_to_bf16(acc[mt][5][i]) << 16);
+                            v.w = f32_to_bf16(acc[mt][6][i]) | (f32_to_bf16(acc[mt][7][i]) << 16);
+                            *reinterpret_cast<uint4*>(dst) = v;
+                        } else {
+#pragma unroll
+                            for (int nt = 0; nt < C::NT; ++nt)
+                                dst[nt] = (uint16_t)f32_to_bf16(acc[mt][nt][i]);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Tile configuration: 256 x 256 output tiles, 4 waves of 128 x 128.
+constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 2;
+
+int gemm_bm() { return kBM; }
+
+template <bool kG1>
+static hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
+    using C = Cfg<kBM, kBN, kWM, kWN, kG1>;
+    auto kern = grouped_gemm_kernel<kBM, kBN, kWM, kWN, kG1>;
+    const size_t lds = C::kStages * (size_t)C::kStage + (size_t)kBM * 8;
+    static bool attr_set = false;
+    static int cus = 0;
+    if (!attr_set) {
+        hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        int dev = 0;
+        if (err == hipSuccess) err = hipGetDevice(&dev);
+        if (err == hipSuccess)
+            err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err != hipSuccess) return err;
+        attr_set = true;
+    }
+    const int ntiles = kG1 ? (2 * p.I) / kBN : (p.H + kBN - 1) / kBN;
+    const int64_t upper = (int64_t)p.max_mtiles * ntiles;
+    const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(upper, cus));
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), lds, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm1(const GemmParams& p, hipStream_t s) { return launch_gemm<true>(p, s); }
+hipError_t launch_gemm2(const GemmParams& p, hipStream_t s) { return launch_gemm<false>(p, s); }
+
+}  // namespace moe

@@ -1,0 +1,79 @@
+// Kernel parameter blocks and launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace moe {
+
+constexpr int kRouteTokensPerBlock = 16;
+
+struct RouteParams {
+    const float* logits;        // [T, E] or null
+    const int32_t* idx_in;      // [T, k] caller ids (when logits == null)
+    const float* w_in;          // [T, k]
+    int32_t* idx_out;           // [T, k]
+    float* w_out;               // [T, k]
+    int* cnt;                   // [E] global counters, zero on entry
+    int32_t* slot_in_e;         // [T, k] slot of the pair inside its expert
+    const uint16_t* x;          // [T, H] BF16 or null (no quantisation)
+    uint8_t* xq;                // [T, H]
+    uint8_t* xsf;               // [T, H/32]
+    int64_t T;
+    int H, E, topk, score_fn, renorm;
+};
+
+struct ScatterParams {
+    const int32_t* idx;         // [T, k]
+    const int32_t* slot_in_e;   // [T, k]
+    int* cnt;                   // [E] global counters (reset to zero by the last block)
+    unsigned* arrive;           // arrival counter (reset to zero by the last block)
+    int32_t* counts_out;        // [E]
+    int32_t* offsets_out;       // [E + 1]
+    int32_t* mtile_off;         // [E + 1] prefix sum of ceil(count / bm)
+    int32_t* mtile_e;           // [sum ceil(count / bm)] expert of each m-tile
+    int32_t* slot_src;          // [T*k]
+    int32_t* slot_of;           // [T, k]
+    int64_t T;
+    int E, topk, bm;
+};
+
+hipError_t launch_route(const RouteParams& rp, const ScatterParams& sp, hipStream_t s);
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* sf,
+                            hipStream_t s);
+hipError_t launch_pack_weights(const uint16_t* w, int64_t rows, int cols, uint8_t* q,
+                               uint8_t* sf, hipStream_t s);
+
+// Grouped GEMMs.  Positions p index the per-expert segments produced by the
+// bucketisation: expert e owns p in [offsets[e], offsets[e+1]).
+struct GemmParams {
+    const int32_t* offsets;     // [E + 1]
+    const int32_t* mtile_off;   // [E + 1] m-tiles per expert, prefix-summed (tile rows = BM)
+    const int32_t* mtile_e;     // [max_mtiles] expert of each m-tile
+    const int32_t* slot_src;    // [R] t*k + j of position p
+    const float* topk_w;        // [T, k]
+    const uint8_t* xq;          // [T, H]    GEMM1 A (gathered rows)
+    const uint8_t* xsf;         // [T, H/32]
+    const uint8_t* w13;         // [E, 2I, H/2]
+    const uint8_t* w13sf;       // [E, 2I, H/32]
+    uint8_t* hq;                // [R, I]    GEMM1 output / GEMM2 A
+    uint8_t* hsf;               // [R, I/32]
+    const uint8_t* w2;          // [E, H, I/2]
+    const uint8_t* w2sf;        // [E, H, I/32]
+    uint16_t* o;                // [R, H]    GEMM2 output (BF16)
+    int64_t T;
+    int H, I, E, topk;
+    int max_mtiles;             // upper bound of mtile_off[E]
+};
+
+int gemm_bm();                  // rows per m-tile of the grouped GEMMs
+hipError_t launch_gemm1(const GemmParams& p, hipStream_t s);
+hipError_t launch_gemm2(const GemmParams& p, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t* o, const int32_t* slot_of, int64_t T, int topk, int H,
+                          uint16_t* y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,92 @@
+// Block quantisers: activations BF16 -> E4M3 + UE8M0/32 ("MegaMoE" notes,
+// "Dispatch阶段") and weights BF16 -> E2M1 + UE8M0/32 along K ("MegaMoE" notes,
+// "Expert矩阵权重量化").  Four lanes share a 32-element group, eight BF16
+// (16 bytes) per lane, so a wave reads 1 KiB of contiguous input per step.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kQuantThreads = 256;
+
+MOE_DEV void load8(const uint16_t* src, float f[8]) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(src);
+    f[0] = bf16_to_f32(raw.x & 0xFFFFu); f[1] = bf16_to_f32(raw.x >> 16);
+    f[2] = bf16_to_f32(raw.y & 0xFFFFu); f[3] = bf16_to_f32(raw.y >> 16);
+    f[4] = bf16_to_f32(raw.z & 0xFFFFu); f[5] = bf16_to_f32(raw.z >> 16);
+    f[6] = bf16_to_f32(raw.w & 0xFFFFu); f[7] = bf16_to_f32(raw.w >> 16);
+}
+
+MOE_DEV float group_amax4(const float f[8]) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf(f[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    return fmaxf(amax, __shfl_xor(amax, 2, 64));
+}
+
+__global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const uint16_t* __restrict__ x,
+                                                                  int64_t tasks, int cols,
+                                                                  uint8_t* __restrict__ q,
+                                                                  uint8_t* __restrict__ sf) {
+    // task i: 8 elements starting at element 8*i of the flattened [rows, cols] array
+    for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < tasks;
+         i += (int64_t)gridDim.x * kQuantThreads) {
+        float f[8];
+        load8(x + i * 8, f);
+        float amax = group_amax4(f);
+        int e = e4m3_block_exp(amax);
+        float inv = exp2_neg(e);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lo |= e4m3_encode(f[j] * inv) << (8 * j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hi |= e4m3_encode(f[4 + j] * inv) << (8 * j);
+        *reinterpret_cast<uint2*>(q + i * 8) = make_uint2(lo, hi);
+        if ((i & 3) == 0) sf[i >> 2] = (uint8_t)(e + 127);
+    }
+}
+
+__global__ __launch_bounds__(kQuantThreads) void pack_weights_kernel(const uint16_t* __restrict__ w,
+                                                                     int64_t tasks,
+                                                                     uint8_t* __restrict__ q,
+                                                                     uint8_t* __restrict__ sf) {
+    for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < tasks;
+         i += (int64_t)gridDim.x * kQuantThreads) {
+        float f[8];
+        load8(w + i * 8, f);
+        float amax = group_amax4(f);
+        int e = e2m1_block_exp(amax);
+        float inv = exp2_neg(e);
+        uint32_t packed = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) packed |= e2m1_encode(f[j] * inv) << (4 * j);
+        reinterpret_cast<uint32_t*>(q)[i] = packed;
+        if ((i & 3) == 0) sf[i >> 2] = (uint8_t)(e + 127);
+    }
+}
+
+static unsigned grid_for(int64_t tasks) {
+    int64_t blocks = (tasks + kQuantThreads - 1) / kQuantThreads;
+    return (unsigned)std::min<int64_t>(std::max<int64_t>(blocks, 1), 65536);
+}
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* sf,
+                            hipStream_t s) {
+    int64_t tasks = rows * (cols / 8);
+    if (tasks == 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_act_kernel, dim3(grid_for(tasks)), dim3(kQuantThreads), 0, s, x,
+                       tasks, cols, q, sf);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_weights(const uint16_t* w, int64_t rows, int cols, uint8_t* q, uint8_t* sf,
+                               hipStream_t s) {
+    int64_t tasks = rows * (cols / 8);
+    if (tasks == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_weights_kernel, dim3(grid_for(tasks)), dim3(kQuantThreads), 0, s, w,
+                       tasks, q, sf);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,295 @@
+// Routing, counting-sort bucketisation and activation quantisation.
+//
+// Launch A (route_count_quant): each workgroup takes a chunk of tokens and
+//   1. routes them: top-k of the float32 logits (softmax and sigmoid are
+//      increasing, so the k best scores are the k largest logits), weights from
+//      softmax or sigmoid, optionally renormalised ("MonoMoe kernel — design"
+//      §1, phase 1); or reads a caller's top-k ids and weights;
+//   2. counts its (token, slot) pairs per expert in an LDS histogram, the LDS
+//      atomic returning each pair's rank inside the workgroup, then adds the
+//      histogram to the global per-expert counters with one atomic per expert,
+//      whose return value is this workgroup's base inside the expert
+//      ("05.10 Counting Sort / Bucketization" 2.1 COUNT, 2.2 PREFIX SUM); the
+//      pair's slot inside its expert is base + rank;
+//   3. quantises its tokens' x rows to E4M3 + UE8M0 per 32.
+// Launch B (scatter): every workgroup scans the final counts into expert
+//   offsets and writes t*k + j to position offsets[e] + slot (2.3 SCATTER) and
+//   the inverse map.  The last workgroup to finish zeroes the global counters,
+//   so the workspace is ready for the next call without a host memset.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kRouteThreads = 256;
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kMaxTopk = 16;
+constexpr int kMaxExperts = 1024;
+
+// (value, index) ordering of the top-k: larger value first, then smaller index.
+MOE_DEV bool better(float v, int i, float ov, int oi) {
+    return v > ov || (v == ov && i < oi);
+}
+
+// Top-k of one token's E logits with one wave.  Lane l owns experts
+// l, l + 64, ...; NPL = values per lane.  Writes idx/w for the token.
+template <int NPL>
+MOE_DEV void route_token(const float* __restrict__ lrow, int E, int k, int score_fn, int renorm,
+                         int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                         float* sel_v, int* sel_i, int* lds_idx) {
+    const int lane = threadIdx.x & 63;
+    float v[NPL];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        int e = lane + 64 * i;
+        v[i] = e < E ? lrow[e] : 0.0f;
+        if (e >= E) taken |= 1u << i;
+    }
+    for (int r = 0; r < k; ++r) {
+        float bv = 0.0f;
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            bool free_ = !((taken >> i) & 1u);
+            if (free_ && (bi == 0x7FFFFFFF || better(v[i], lane + 64 * i, bv, bi))) {
+                bv = v[i];
+                bi = lane + 64 * i;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            float ov = __shfl_xor(bv, o, 64);
+            int oi = __shfl_xor(bi, o, 64);
+            if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi))) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if (lane == 0) {
+            sel_v[r] = bv;
+            sel_i[r] = bi;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // weights
+    float lmax = sel_v[0];
+    float s = 0.0f;
+    if (lane < k) {
+        float lv = sel_v[lane];
+        s = score_fn == 0 ? expf(lv - lmax) : 1.0f / (1.0f + expf(-lv));
+    }
+    float denom = 1.0f;
+    if (renorm) {
+        denom = wave_sum(s);
+    } else if (score_fn == 0) {
+        float z = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i)
+            if (lane + 64 * i < E) z += expf(v[i] - lmax);
+        denom = wave_sum(z);
+    }
+    if (lane < k) {
+        idx_out[lane] = sel_i[lane];
+        lds_idx[lane] = sel_i[lane];
+        w_out[lane] = s / denom;
+    }
+}
+
+template <int NPL>
+__global__ __launch_bounds__(kRouteThreads) void route_count_quant_kernel(RouteParams p) {
+    __shared__ int hist[kMaxExperts];
+    __shared__ int base[kMaxExperts];
+    __shared__ float sel_v[kRouteWaves][kMaxTopk];
+    __shared__ int sel_i[kRouteWaves][kMaxTopk];
+    __shared__ int pair_rank[kRouteTokensPerBlock * kMaxTopk];
+    __shared__ int pair_exp[kRouteTokensPerBlock * kMaxTopk];   // expert of pair i of this block
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int64_t t0 = (int64_t)blockIdx.x * kRouteTokensPerBlock;
+    const int ntok = (int)min<int64_t>(kRouteTokensPerBlock, p.T - t0);
+    const int k = p.topk;
+
+    for (int e = tid; e < p.E; e += kRouteThreads) hist[e] = 0;
+
+    // 1. routing (one wave per token) or caller's ids
+    if (p.logits) {
+        for (int i = wave; i < ntok; i += kRouteWaves) {
+            int64_t t = t0 + i;
+            route_token<NPL>(p.logits + t * p.E, p.E, k, p.score_fn, p.renorm,
+                             p.idx_out + t * k, p.w_out + t * k, sel_v[wave], sel_i[wave],
+                             pair_exp + i * k);
+        }
+    } else {
+        for (int i = tid; i < ntok * k; i += kRouteThreads) {
+            int e = p.idx_in[t0 * k + i];
+            pair_exp[i] = e;
+            if (p.idx_in != p.idx_out) {
+                p.idx_out[t0 * k + i] = e;
+                p.w_out[t0 * k + i] = p.w_in[t0 * k + i];
+            }
+        }
+    }
+    __syncthreads();
+
+    // 2. count: LDS histogram; the LDS atomic's return is the pair's rank here
+    const int npairs = ntok * k;
+    for (int i = tid; i < npairs; i += kRouteThreads) {
+        int e = pair_exp[i];
+        pair_rank[i] = (e >= 0 && e < p.E) ? atomicAdd(&hist[e], 1) : -1;
+    }
+    __syncthreads();
+    for (int e = tid; e < p.E; e += kRouteThreads) {
+        int c = hist[e];
+        base[e] = c ? atomicAdd(&p.cnt[e], c) : 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < npairs; i += kRouteThreads) {
+        int e = pair_exp[i];
+        p.slot_in_e[t0 * k + i] = pair_rank[i] >= 0 ? base[e] + pair_rank[i] : -1;
+    }
+
+    // 3. activation quantisation: 4 lanes per 32-element group, 8 BF16 per lane
+    if (p.x) {
+        const int groups_per_row = p.H / kGroup;
+        const int tasks = ntok * groups_per_row * 4;
+        for (int i = tid; i < tasks; i += kRouteThreads) {
+            int q = i & 3;
+            int g = i >> 2;
+            int r = g / groups_per_row;
+            int gc = g - r * groups_per_row;
+            int64_t t = t0 + r;
+            const uint4 raw = *reinterpret_cast<const uint4*>(p.x + t * p.H + gc * kGroup + q * 8);
+            float f[8];
+            f[0] = bf16_to_f32(raw.x & 0xFFFFu); f[1] = bf16_to_f32(raw.x >> 16);
+            f[2] = bf16_to_f32(raw.y & 0xFFFFu); f[3] = bf16_to_f32(raw.y >> 16);
+            f[4] = bf16_to_f32(raw.z & 0xFFFFu); f[5] = bf16_to_f32(raw.z >> 16);
+            f[6] = bf16_to_f32(raw.w & 0xFFFFu); f[7] = bf16_to_f32(raw.w >> 16);
+            float amax = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf(f[j]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+            int e = e4m3_block_exp(amax);
+            float inv = exp2_neg(e);
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) lo |= e4m3_encode(f[j] * inv) << (8 * j);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hi |= e4m3_encode(f[4 + j] * inv) << (8 * j);
+            *reinterpret_cast<uint2*>(p.xq + t * p.H + gc * kGroup + q * 8) = make_uint2(lo, hi);
+            if (q == 0) p.xsf[t * groups_per_row + gc] = (uint8_t)(e + 127);
+        }
+    }
+}
+
+// Exclusive scan of n <= 1024 ints in LDS by a 256-thread block: out[0..n].
+MOE_DEV void block_exclusive_scan(const int* in, int* out, int n, int* tmp) {
+    const int tid = threadIdx.x;
+    int v[4];
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int i = tid * 4 + j;
+        v[j] = i < n ? in[i] : 0;
+        s += v[j];
+    }
+    tmp[tid] = s;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        int a = tid >= o ? tmp[tid - o] : 0;
+        __syncthreads();
+        tmp[tid] += a;
+        __syncthreads();
+    }
+    int run = tmp[tid] - s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int i = tid * 4 + j;
+        if (i < n) out[i] = run;
+        run += v[j];
+    }
+    if (tid == 255) out[n] = tmp[255];
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p) {
+    __shared__ int cnt[kMaxExperts];
+    __shared__ int off[kMaxExperts + 1];
+    __shared__ int tiles[kMaxExperts];
+    __shared__ int toff[kMaxExperts + 1];
+    __shared__ int tmp[256];
+    __shared__ int last;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < p.E; e += kRouteThreads)
+        cnt[e] = __hip_atomic_load(&p.cnt[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    // every counter has been read by this block: report it, the last block resets them
+    if (tid == 0) {
+        __threadfence();
+        unsigned prev = atomicAdd(p.arrive, 1u);
+        last = prev == gridDim.x - 1;
+    }
+    block_exclusive_scan(cnt, off, p.E, tmp);
+    if (last) {
+        for (int e = tid; e < p.E; e += kRouteThreads) p.cnt[e] = 0;
+        if (tid == 0) *p.arrive = 0;
+    }
+    if (blockIdx.x == 0) {
+        for (int e = tid; e < p.E; e += kRouteThreads) tiles[e] = ceil_div(cnt[e], p.bm);
+        __syncthreads();
+        block_exclusive_scan(tiles, toff, p.E, tmp);
+        for (int e = tid; e < p.E; e += kRouteThreads) {
+            p.counts_out[e] = cnt[e];
+            for (int m = toff[e]; m < toff[e + 1]; ++m) p.mtile_e[m] = e;
+        }
+        for (int e = tid; e <= p.E; e += kRouteThreads) {
+            p.offsets_out[e] = off[e];
+            p.mtile_off[e] = toff[e];
+        }
+    }
+    const int64_t npairs = p.T * p.topk;
+    for (int64_t i = (int64_t)blockIdx.x * kRouteThreads + tid; i < npairs;
+         i += (int64_t)gridDim.x * kRouteThreads) {
+        int e = p.idx[i];
+        int s = p.slot_in_e[i];
+        if (e >= 0 && e < p.E && s >= 0) {
+            int pos = off[e] + s;
+            p.slot_src[pos] = (int)i;
+            p.slot_of[i] = pos;
+        } else {
+            p.slot_of[i] = -1;
+        }
+    }
+}
+
+hipError_t launch_route(const RouteParams& rp, const ScatterParams& sp, hipStream_t s) {
+    if (rp.T > 0) {
+        dim3 grid((unsigned)((rp.T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock));
+        int npl = (rp.E + 63) / 64;
+        if (!rp.logits) npl = 1;
+        if (npl <= 1)
+            hipLaunchKernelGGL(route_count_quant_kernel<1>, grid, dim3(kRouteThreads), 0, s, rp);
+        else if (npl <= 2)
+            hipLaunchKernelGGL(route_count_quant_kernel<2>, grid, dim3(kRouteThreads), 0, s, rp);
+        else if (npl <= 4)
+            hipLaunchKernelGGL(route_count_quant_kernel<4>, grid, dim3(kRouteThreads), 0, s, rp);
+        else if (npl <= 8)
+            hipLaunchKernelGGL(route_count_quant_kernel<8>, grid, dim3(kRouteThreads), 0, s, rp);
+        else
+            hipLaunchKernelGGL(route_count_quant_kernel<16>, grid, dim3(kRouteThreads), 0, s, rp);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    int64_t npairs = sp.T * sp.topk;
+    unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(1024, (npairs + 1023) / 1024));
+    hipLaunchKernelGGL(scatter_kernel, dim3(blocks), dim3(kRouteThreads), 0, s, sp);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,211 @@
+"""GPU parity of the HIP path against the CPU oracle (through the C ABI).
+
+Integer outputs (routing ids, counts, offsets, slot multisets, FP8/FP4 codes
+and scales from the quantisers) must be bit-exact; floating-point outputs meet
+the tolerances stated in tests/gpu_common.py.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as W
+from oracle import codecs as C
+from oracle import moe_ref as M
+from tests import gpu_common as G
+
+pytestmark = pytest.mark.gpu
+
+# several m-tiles per expert with ragged tails, a partial GEMM2 n-tile (H % 256 != 0),
+# three GEMM1 n-tiles, T not a multiple of the routing chunk
+RAGGED = W.Workload("ragged", T=601, H=640, I=384, E=5, topk=2)
+SMALL_SHAPES = [W.WORKLOADS["tiny"], RAGGED,
+                W.Workload("k1", T=77, H=256, I=128, E=3, topk=1),
+                W.Workload("sig", T=130, H=384, I=256, E=16, topk=4, score_fn=W.SIGMOID),
+                W.Workload("t1", T=1, H=128, I=128, E=4, topk=2)]
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _oracle_full(w, topk=None):
+    x = W.gen_x(w)
+    wq = G.oracle_weights(w)
+    if topk is None:
+        return M.forward(x, *wq, topk=w.topk, I=w.I, logits=W.gen_logits(w),
+                         score_fn=w.score_fn, renorm=bool(w.renorm))
+    return M.forward(x, *wq, topk=w.topk, I=w.I, topk_idx=topk[0], topk_w=topk[1])
+
+
+# ------------------------------------------------------------------ quantisers
+
+@pytest.mark.parametrize("rows,cols", [(64, 256), (5, 2048), (333, 7168)])
+def test_quant_act_bit_exact(rows, cols):
+    _log(f"quant_act {rows}x{cols}")
+    w = W.Workload("q", T=rows, H=cols, I=128, E=1, topk=1)
+    x = W.gen_x(w)
+    q, sf = G.lib().quant_act(G.bf16_dev(x))
+    torch.cuda.synchronize()
+    rq, rsf = M.quant_act(x)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(sf.cpu().numpy(), rsf)
+
+
+def test_quant_act_special_values():
+    _log("quant_act special values")
+    vals = np.zeros((4, 64), np.float32)
+    vals[1, :32] = np.array([448.0, -464.0, 2.0 ** -10, -(2.0 ** -9)] * 8)    # clamp / ties / subnormal
+    vals[2, :] = -0.0
+    vals[3, :] = np.ldexp(1.0, np.arange(64) % 40 - 20) * (1.75 + 2.0 ** -7)
+    x = W.to_bf16_bits(vals)
+    q, sf = G.lib().quant_act(G.bf16_dev(x))
+    torch.cuda.synchronize()
+    rq, rsf = M.quant_act(x)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(sf.cpu().numpy(), rsf)
+
+
+@pytest.mark.parametrize("rows,cols", [(256, 256), (1024, 2048), (4096, 7168)])
+def test_pack_weights_bit_exact(rows, cols):
+    _log(f"pack_weights {rows}x{cols}")
+    w = W.Workload("p", T=1, H=cols, I=rows // 2, E=1, topk=1)
+    wb = W.gen_expert_w13(w, 0)[:rows]
+    q, sf = G.lib().pack_weights(G.bf16_dev(wb))
+    torch.cuda.synchronize()
+    rq, rsf = M.pack_weights(wb)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(sf.cpu().numpy(), rsf)
+
+
+# ------------------------------------------------------------------ routing
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_route_bit_exact(name):
+    w = W.WORKLOADS[name]
+    _log(f"route {name}")
+    m = G.lib()
+    d = m.dims(w.T, w.H, w.I, w.E, w.topk, w.score_fn, w.renorm)
+    ws = m.new_workspace(d)
+    logits = W.gen_logits(w)
+    out = m.route(d, G.to_dev(logits), ws)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    idx, wt = M.route(logits, w.topk, w.score_fn, bool(w.renorm))
+    assert np.array_equal(got["topk_idx"], idx)
+    np.testing.assert_allclose(got["topk_w"], wt, rtol=4e-6, atol=1e-7)
+    G.check_bucketize(got, idx, w.E)
+    # the counters were reset: a second call on the same workspace gives the same counts
+    out2 = m.route(d, G.to_dev(logits), ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2["counts"].cpu().numpy(), got["counts"])
+
+
+# ------------------------------------------------------------------ whole layer
+
+@pytest.mark.parametrize("w", SMALL_SHAPES, ids=lambda w: w.name)
+def test_forward_matches_oracle(w):
+    _log(f"forward {w.name}")
+    dl = G.DeviceLayer(w)
+    y = dl.forward()
+    inter = dl.intermediates()
+    ref = _oracle_full(w)
+    assert np.array_equal(inter["topk_idx"], ref["topk_idx"])
+    G.check_bucketize(inter, ref["topk_idx"], w.E)
+    assert np.array_equal(inter["xq"], ref["xq"])
+    assert np.array_equal(inter["xsf"], ref["xsf"])
+    # hq by (t, j): map GPU positions and oracle positions through slot_of
+    so_g = inter["slot_of"].reshape(-1)
+    so_r = ref["slot_of"].reshape(-1)
+    G.check_hq(inter["hq"][so_g], inter["hsf"][so_g], ref["hq"][so_r], ref["hsf"][so_r])
+    G.check_y(G.y_bits(y), ref["y"])
+
+
+def test_forward_decode_matches_oracle():
+    w = W.WORKLOADS["decode"]
+    _log("forward decode")
+    dl = G.DeviceLayer(w)
+    y = dl.forward()
+    ref = _oracle_full(w)
+    inter = dl.intermediates()
+    so_g, so_r = inter["slot_of"].reshape(-1), ref["slot_of"].reshape(-1)
+    G.check_hq(inter["hq"][so_g], inter["hsf"][so_g], ref["hq"][so_r], ref["hsf"][so_r])
+    G.check_y(G.y_bits(y), ref["y"])
+
+
+@pytest.mark.parametrize("name", ["dsv3_prefill", "dsv3_skewed"])
+def test_forward_full_size_sampled_tokens(name):
+    """Full-size launch; the oracle recomputes a sample of tokens one by one."""
+    w = W.WORKLOADS[name]
+    _log(f"forward {name} (sampled)")
+    dl = G.DeviceLayer(w)
+    y = dl.forward()
+    inter = dl.intermediates()
+    logits = dl.logits_np
+    idx, _ = M.route(logits, w.topk, w.score_fn, bool(w.renorm))
+    assert np.array_equal(inter["topk_idx"], idx)
+    G.check_bucketize(inter, idx, w.E)
+    toks = [0, w.T - 1]
+    ref = M.forward(dl.x_np, *G.oracle_weights(w), topk=w.topk, I=w.I, logits=logits,
+                    tokens=toks)
+    G.check_y(G.y_bits(y), ref["y"], rows=toks)
+    so_g = inter["slot_of"][toks].reshape(-1)
+    so_r = ref["slot_of"][toks].reshape(-1)
+    G.check_hq(inter["hq"][so_g], inter["hsf"][so_g], ref["hq"][so_r], ref["hsf"][so_r])
+    # every output row is finite and the untouched workspace regions stay consistent
+    assert torch.isfinite(y.float()).all()
+
+
+def test_forward_external_topk_with_masked_slots():
+    w = W.Workload("ext", T=257, H=256, I=256, E=6, topk=3)
+    _log("forward external topk")
+    topk = W.gen_external_topk(w, mask_frac=0.25)
+    dl = G.DeviceLayer(w, external_topk=topk)
+    y = dl.forward(use_logits=False)
+    ref = _oracle_full(w, topk)
+    inter = dl.intermediates()
+    G.check_bucketize(inter, topk[0], w.E)
+    G.check_y(G.y_bits(y), ref["y"])
+
+
+def test_forward_all_tokens_one_expert():
+    w = W.Workload("hot", T=700, H=256, I=128, E=8, topk=1)
+    _log("forward one hot expert")
+    idx = np.full((w.T, 1), 5, np.int32)
+    wt = np.ones((w.T, 1), np.float32)
+    dl = G.DeviceLayer(w, external_topk=(idx, wt))
+    y = dl.forward(use_logits=False)
+    ref = _oracle_full(w, (idx, wt))
+    G.check_y(G.y_bits(y), ref["y"])
+
+
+def test_forward_is_deterministic_and_workspace_reusable():
+    w = RAGGED
+    _log("determinism")
+    dl = G.DeviceLayer(w)
+    ys = [G.y_bits(dl.forward()) for _ in range(3)]
+    assert all(np.array_equal(ys[0], v) for v in ys[1:])
+    # a smaller call on the same workspace, then the full call again
+    m = G.lib()
+    d_small = m.dims(100, w.H, w.I, w.E, w.topk)
+    y_small = m.forward(d_small, dl.x[:100], dl.w13q, dl.w13sf, dl.w2q, dl.w2sf, dl.ws,
+                        logits=dl.logits[:100])
+    torch.cuda.synchronize()
+    ref_small = M.forward(dl.x_np[:100], *G.oracle_weights(w), topk=w.topk, I=w.I,
+                          logits=dl.logits_np[:100])
+    G.check_y(G.y_bits(y_small), ref_small["y"])
+    assert np.array_equal(G.y_bits(dl.forward()), ys[0])
+
+
+def test_forward_zero_tokens_is_noop():
+    m = G.lib()
+    d = m.dims(0, 256, 128, 4, 2)
+    ws = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    x = torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((1, 256), 7.0, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    m.forward_raw(m.forward_args(d, x, w, w, w, w, y, ws, logits=x))
+    torch.cuda.synchronize()
+    assert (y.float() == 7.0).all()
