@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--cpu-sample-tokens", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="before the timed steps, copy a buffer of this many MiB once (a "
+                         "plain copy kernel of known size, to calibrate traffic counters)")
     ap.add_argument("--flush-mb", type=int, default=0,
                     help="write this many MiB between steps (outside the timed events) to "
                          "evict the last-level cache; 0 = off")
@@ -140,6 +143,13 @@ def main():
     args_ev = [m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, stage_events=e)
                for e in ev]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    if a.calib_copy_mb:
+        src = torch.ones(a.calib_copy_mb << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(a.warmup):
         m.forward_raw(args_plain, stream)

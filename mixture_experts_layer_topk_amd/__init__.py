@@ -13,7 +13,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe.so")
+# MOE_LIB_PATH selects another build of the same library (e.g. a profiling build)
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1

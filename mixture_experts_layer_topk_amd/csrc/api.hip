@@ -2,7 +2,7 @@
 // workspace carve, and the launch sequence of the layer.
 #include <string>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "common.h"
 #include "kernels.h"
 

@@ -9,6 +9,7 @@
 namespace moe {
 
 constexpr int kCombineThreads = 256;
+constexpr int kMaxSlots = 16;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t* __restrict__ o,
                                                                   const int32_t* __restrict__ slot_of,
@@ -19,15 +20,23 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
          i += (int64_t)gridDim.x * kCombineThreads) {
         int64_t t = i / cpr;
         int c = (int)(i - t * cpr) * 8;
+        // all of the token's slot rows are fetched before any is added
+        int pos[kMaxSlots];
+#pragma unroll
+        for (int j = 0; j < kMaxSlots; ++j) pos[j] = j < topk ? slot_of[t * topk + j] : -1;
+        uint4 raw[kMaxSlots];
+#pragma unroll
+        for (int j = 0; j < kMaxSlots; ++j)
+            raw[j] = pos[j] >= 0 ? *reinterpret_cast<const uint4*>(o + (int64_t)pos[j] * H + c)
+                                 : make_uint4(0, 0, 0, 0);
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int j = 0; j < topk; ++j) {
-            int p = slot_of[t * topk + j];
-            if (p < 0) continue;
-            const uint4 raw = *reinterpret_cast<const uint4*>(o + (int64_t)p * H + c);
-            acc[0] += bf16_to_f32(raw.x & 0xFFFFu); acc[1] += bf16_to_f32(raw.x >> 16);
-            acc[2] += bf16_to_f32(raw.y & 0xFFFFu); acc[3] += bf16_to_f32(raw.y >> 16);
-            acc[4] += bf16_to_f32(raw.z & 0xFFFFu); acc[5] += bf16_to_f32(raw.z >> 16);
-            acc[6] += bf16_to_f32(raw.w & 0xFFFFu); acc[7] += bf16_to_f32(raw.w >> 16);
+#pragma unroll
+        for (int j = 0; j < kMaxSlots; ++j) {
+            if (pos[j] < 0) continue;
+            acc[0] += bf16_to_f32(raw[j].x & 0xFFFFu); acc[1] += bf16_to_f32(raw[j].x >> 16);
+            acc[2] += bf16_to_f32(raw[j].y & 0xFFFFu); acc[3] += bf16_to_f32(raw[j].y >> 16);
+            acc[4] += bf16_to_f32(raw[j].z & 0xFFFFu); acc[5] += bf16_to_f32(raw[j].z >> 16);
+            acc[6] += bf16_to_f32(raw[j].w & 0xFFFFu); acc[7] += bf16_to_f32(raw[j].w >> 16);
         }
         uint4 out;
         out.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);

@@ -41,8 +41,10 @@
 // Loads go straight from global memory to LDS (global_load_lds_dwordx4): one
 // instruction fills 1 KiB of LDS contiguously, lane l landing at byte 16 l, so
 // the XOR swizzle of the LDS tiles is applied on the global side by choosing
-// which 16-byte chunk each lane fetches.  Three LDS stages are in flight: the
-// loads of step ks + 2 are issued while step ks is multiplied.
+// which 16-byte chunk each lane fetches.  Three LDS stages rotate: the loads
+// of step ks + 3 are issued in the middle of step ks, two steps ahead of use.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -77,10 +79,18 @@ struct Cfg {
     static_assert(kLoads < 64, "vmcnt range");
 };
 
+// LDS swizzles.  A fragment read touches 16 consecutive rows at one logical
+// 16-byte chunk; B the same for 16 consecutive rows of 64 bytes.  The XOR
+// patterns below put those 16 reads on distinct 16-byte bank slots both within
+// each 8-lane half (128-byte window) and across all 16 lanes (256-byte window).
+// Both depend on the row modulo 16 only, so the fragments of different m-tiles
+// (n-tiles) sit at constant offsets from one another.
+MOE_DEV int a_swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
+MOE_DEV int b_swz(int n) { return ((n >> 1) ^ ((n >> 3) & 1)) & 3; }
 // A: row r, 16-byte chunk c (of 8) -> swizzled byte offset inside the A tile.
-MOE_DEV int a_off(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 4); }
+MOE_DEV int a_off(int r, int c) { return r * BK + ((c ^ a_swz(r)) << 4); }
 // B: row n, 16-byte chunk c (of 4) -> swizzled byte offset inside the B tile.
-MOE_DEV int b_off(int n, int c) { return n * (BK / 2) + ((c ^ ((n >> 2) & 3)) << 4); }
+MOE_DEV int b_off(int n, int c) { return n * (BK / 2) + ((c ^ b_swz(n)) << 4); }
 
 MOE_DEV v4f mfma_fp8_fp4(const v8i& a, const v4i& b, const v4f& c, int sa, int sb) {
     v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
@@ -123,10 +133,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
     __shared__ int s_tile[4];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const int l16 = lane & 15, lg = lane >> 4;
 
     const int K = kG1 ? p.H : p.I;                 // reduction length
     const int nk = K / BK;
@@ -140,6 +146,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
     const int total = s_tile[3] * NTILES;
 
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+        // Per-lane indices are re-derived from an opaque copy of the thread id in
+        // every tile, so the compiler recomputes the (cheap) per-lane constants
+        // here instead of keeping dozens of them alive across the K loop.
+        int tid_v = tid;
+        asm volatile("" : "+v"(tid_v));
+        const int lane = tid_v & 63;
+        const int wave = tid_v >> 6;
+        const int wm = wave / WN, wn = wave % WN;
+        const int l16 = lane & 15, lg = lane >> 4;
         const int mt_g = tile / NTILES;
         const int ntile = tile - mt_g * NTILES;
         if (tid == 0) {
@@ -186,52 +201,52 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
         const uint8_t* wsf_base = kG1 ? p.w13sf + (int64_t)e * (2 * p.I) * sf_stride
                                       : p.w2sf + (int64_t)e * p.H * sf_stride;
 
-        // per-lane global sources of each load instruction (fixed over K)
-        const uint8_t* a_src[C::kAI];
+        // per-lane global sources of each load instruction (fixed over K), as
+        // 32-bit byte offsets from wave-uniform bases
+        uint32_t a_src[C::kAI];
 #pragma unroll
         for (int j = 0; j < C::kAI; ++j) {
             int r = 8 * (j * C::kWaves + wave) + (lane >> 3);
-            int c = (lane & 7) ^ ((r >> 1) & 7);
-            a_src[j] = a_base + (int64_t)s_tok[r] * K + c * 16;
+            int c = (lane & 7) ^ a_swz(r);
+            a_src[j] = (uint32_t)s_tok[r] * (uint32_t)K + c * 16;
         }
-        const uint8_t* b_src[C::kBI];
+        uint32_t b_src[C::kBI];
 #pragma unroll
         for (int j = 0; j < C::kBI; ++j) {
             int n = 16 * (j * C::kWaves + wave) + (lane >> 2);
-            int c = (lane & 3) ^ ((n >> 2) & 3);
-            b_src[j] = w_base + (int64_t)b_row(n) * b_stride + c * 16;
+            int c = (lane & 3) ^ b_swz(n);
+            b_src[j] = (uint32_t)b_row(n) * (uint32_t)b_stride + c * 16;
         }
-        const uint8_t* sa_src[C::kSAI];
+        uint32_t sa_src[C::kSAI];
 #pragma unroll
-        for (int j = 0; j < C::kSAI; ++j) {
-            int r = 64 * (j * C::kWaves + wave) + lane;
-            sa_src[j] = sa_base + (int64_t)s_tok[r] * sf_stride;
-        }
-        const uint8_t* sb_src[C::kSBI];
+        for (int j = 0; j < C::kSAI; ++j)
+            sa_src[j] = (uint32_t)s_tok[64 * (j * C::kWaves + wave) + lane] * (uint32_t)sf_stride;
+        uint32_t sb_src[C::kSBI];
 #pragma unroll
-        for (int j = 0; j < C::kSBI; ++j) {
-            int n = 64 * (j * C::kWaves + wave) + lane;
-            sb_src[j] = wsf_base + (int64_t)b_row(n) * sf_stride;
-        }
+        for (int j = 0; j < C::kSBI; ++j)
+            sb_src[j] = (uint32_t)b_row(64 * (j * C::kWaves + wave) + lane) * (uint32_t)sf_stride;
 
-        auto issue = [&](int ks) {
-            uint8_t* sA = smem + (ks % C::kStages) * C::kStage;
+        auto issue = [&](int ks, int stage) {   // K slice ks into LDS stage
+            uint8_t* sA = smem + stage * C::kStage;
             uint8_t* sB = sA + C::kABytes;
             uint8_t* sSA = sB + C::kBBytes;
             uint8_t* sSB = sSA + C::kSABytes;
-            const int ka = ks * BK, kb = ks * (BK / 2), kg = ks * (BK / kGroup);
+            const uint8_t* ga = a_base + ks * BK;
+            const uint8_t* gb = w_base + ks * (BK / 2);
+            const uint8_t* gsa = sa_base + ks * (BK / kGroup);
+            const uint8_t* gsb = wsf_base + ks * (BK / kGroup);
 #pragma unroll
             for (int j = 0; j < C::kAI; ++j)
-                load_lds16(a_src[j] + ka, sA + (j * C::kWaves + wave) * 1024);
+                load_lds16(ga + a_src[j], sA + (j * C::kWaves + wave) * 1024);
 #pragma unroll
             for (int j = 0; j < C::kBI; ++j)
-                load_lds16(b_src[j] + kb, sB + (j * C::kWaves + wave) * 1024);
+                load_lds16(gb + b_src[j], sB + (j * C::kWaves + wave) * 1024);
 #pragma unroll
             for (int j = 0; j < C::kSAI; ++j)
-                load_lds4(sa_src[j] + kg, sSA + (j * C::kWaves + wave) * 256);
+                load_lds4(gsa + sa_src[j], sSA + (j * C::kWaves + wave) * 256);
 #pragma unroll
             for (int j = 0; j < C::kSBI; ++j)
-                load_lds4(sb_src[j] + kg, sSB + (j * C::kWaves + wave) * 256);
+                load_lds4(gsb + sb_src[j], sSB + (j * C::kWaves + wave) * 256);
         };
 
         v4f acc[C::MT][C::NT];
@@ -240,38 +255,88 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
 #pragma unroll
             for (int j = 0; j < C::NT; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-        wait_vmcnt<0>();
-        issue(0);
-        if (nk > 1) issue(1);
-        for (int ks = 0; ks < nk; ++ks) {
-            // stage ks landed (the loads of ks + 1 may still be in flight)
-            if (ks + 1 < nk) wait_vmcnt<C::kLoads>(); else wait_vmcnt<0>();
-            barrier_nofence();          // every lane's stage-ks data; stage (ks+2)%3 no longer read
-            if (ks + 2 < nk) issue(ks + 2);
-            const uint8_t* sA = smem + (ks % C::kStages) * C::kStage;
-            const uint8_t* sB = sA + C::kABytes;
-            const uint8_t* sSA = sB + C::kBBytes;
-            const uint8_t* sSB = sSA + C::kSABytes;
-            v4i bf[C::NT];
-            int sbv[C::NT];
+        // MFMA operands.  Fragment addresses of different tiles differ by
+        // constants (the swizzles depend on row % 16 only).
+        const int a_row0 = wm * C::WTM + l16;
+        const int b_row0 = wn * C::WTN + l16;
+        const int a_lo = a_off(a_row0, lg), a_hi = a_off(a_row0, 4 + lg);
+        const int b_fr = C::kABytes + b_off(b_row0, lg);
+        const int sa_fr = C::kABytes + C::kBBytes + a_row0 * 4 + lg;
+        const int sb_fr = C::kABytes + C::kBBytes + C::kSABytes + b_row0 * 4 + lg;
+        constexpr int MH = C::MT / 2;
+        static_assert(C::MT % 2 == 0 && MH <= C::NT, "A refill spread over the n-tiles");
+        v8i a[C::MT];
+        int sa[C::MT];
+        v4i b[C::NT];
+        int sb[C::NT];
+        auto read_a = [&](const uint8_t* st, int mt) {
+            v4i lo = *reinterpret_cast<const v4i*>(st + a_lo + mt * 16 * BK);
+            v4i hi = *reinterpret_cast<const v4i*>(st + a_hi + mt * 16 * BK);
+            a[mt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            sa[mt] = st[sa_fr + mt * 64];
+        };
+        auto read_b = [&](const uint8_t* st, int nt) {
+            b[nt] = *reinterpret_cast<const v4i*>(st + b_fr + nt * 16 * (BK / 2));
+            sb[nt] = st[sb_fr + nt * 64];
+        };
+        auto mma = [&](int mt, int nt) {
+            acc[mt][nt] = mfma_fp8_fp4(a[mt], b[nt], acc[mt][nt], sa[mt], sb[nt]);
+        };
+
+        // One K step, in two halves, every operand register refilled right after
+        // its last use.  On entry the registers hold step ks's B fragments and
+        // the A fragments of m-tiles [0, MT/2).
+        //  first half  m-tiles [0, MT/2), m-major; meanwhile A of m-tiles
+        //              [MT/2, MT) of step ks is read from stage ks;
+        //  barrier     stage ks is fully in registers and is retired; stage
+        //              ks + 1 is published; the loads of step ks + 3 go into the
+        //              retired stage (the last steps reload the final K slice,
+        //              which the L2 still holds, so the body has no branches);
+        //  second half m-tiles [MT/2, MT), n-major; B of n-tile nt and A of
+        //              m-tile nt < MT/2 of step ks + 1 are read from stage ks + 1
+        //              as soon as n-tile nt is done.  On the last step these
+        //              reads fetch a stage nobody uses.
+        auto step = [&](int ks) {
+            const uint8_t* cur = smem + (ks % C::kStages) * C::kStage;
+            const uint8_t* nxt = smem + ((ks + 1) % C::kStages) * C::kStage;
+#pragma unroll
+            for (int mt = 0; mt < MH; ++mt) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int nt = 0; nt < C::NT; ++nt) mma(mt, nt);
+                __builtin_amdgcn_sched_barrier(0);
+                read_a(cur, MH + mt);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));  // lgkmcnt(0)
+            wait_vmcnt<C::kLoads>();
+            barrier_nofence();
+            issue(min(ks + 3, nk - 1), (ks + 3) % C::kStages);
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt) {
-                int n = wn * C::WTN + nt * 16 + l16;
-                bf[nt] = *reinterpret_cast<const v4i*>(sB + b_off(n, lg));
-                sbv[nt] = sSB[n * 4 + lg];
-            }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int mt = 0; mt < C::MT; ++mt) {
-                int r = wm * C::WTM + mt * 16 + l16;
-                v4i lo = *reinterpret_cast<const v4i*>(sA + a_off(r, lg));
-                v4i hi = *reinterpret_cast<const v4i*>(sA + a_off(r, 4 + lg));
-                v8i af = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                int sav = sSA[r * 4 + lg];
-#pragma unroll
-                for (int nt = 0; nt < C::NT; ++nt)
-                    acc[mt][nt] = mfma_fp8_fp4(af, bf[nt], acc[mt][nt], sav, sbv[nt]);
+                for (int mt = MH; mt < C::MT; ++mt) mma(mt, nt);
+                __builtin_amdgcn_sched_barrier(0);
+                read_b(nxt, nt);
+                if (nt < MH) read_a(nxt, nt);
             }
-        }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        wait_vmcnt<0>();
+        issue(0, 0);
+        issue(min(1, nk - 1), 1);
+        issue(min(2, nk - 1), 2);
+        wait_vmcnt<2 * C::kLoads>();
+        barrier_nofence();
+#pragma unroll
+        for (int mt = 0; mt < MH; ++mt) read_a(smem, mt);
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) read_b(smem, nt);
+        for (int ks = 0; ks < nk; ++ks) step(ks);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));  // lgkmcnt(0)
 
         // ---------------------------------------------------------------- epilogue
         if (kG1) {
@@ -281,6 +346,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
             const int icol0 = ntile * (BN / 2) + wn * (C::WTN / 2);
 #pragma unroll
             for (int mt = 0; mt < C::MT; ++mt) {
+                // one m-tile at a time: keeps the accumulators in AGPRs until used
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = wm * C::WTM + mt * 16 + 4 * lg + i;
@@ -321,6 +388,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
             const int n0 = ntile * BN + wn * C::WTN + l16 * C::NT;
 #pragma unroll
             for (int mt = 0; mt < C::MT; ++mt) {
+                // one m-tile at a time: keeps the accumulators in AGPRs until used
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = wm * C::WTM + mt * 16 + 4 * lg + i;

@@ -99,8 +99,49 @@ MOE_DEV void route_token(const float* __restrict__ lrow, int E, int k, int score
     }
 }
 
-template <int NPL>
-__global__ __launch_bounds__(kRouteThreads) void route_count_quant_kernel(RouteParams p) {
+// Quantise x rows [T, H]: task i covers 8 elements of the flattened array.
+MOE_DEV void quant_rows(const RouteParams& p) {
+    const int64_t tasks = p.T * (p.H / 8);
+    const int64_t stride = (int64_t)gridDim.x * kRouteThreads;
+    constexpr int U = 4;
+    for (int64_t i0 = (int64_t)blockIdx.x * kRouteThreads + threadIdx.x; i0 < tasks; i0 += U * stride) {
+        uint4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int64_t i = i0 + u * stride;
+            raw[u] = i < tasks ? *reinterpret_cast<const uint4*>(p.x + i * 8) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int64_t i = i0 + u * stride;
+            float f[8];
+            f[0] = bf16_to_f32(raw[u].x & 0xFFFFu); f[1] = bf16_to_f32(raw[u].x >> 16);
+            f[2] = bf16_to_f32(raw[u].y & 0xFFFFu); f[3] = bf16_to_f32(raw[u].y >> 16);
+            f[4] = bf16_to_f32(raw[u].z & 0xFFFFu); f[5] = bf16_to_f32(raw[u].z >> 16);
+            f[6] = bf16_to_f32(raw[u].w & 0xFFFFu); f[7] = bf16_to_f32(raw[u].w >> 16);
+            float amax = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf(f[j]));
+            // the 4 lanes of a group are consecutive and share the predicate i < tasks
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+            if (i < tasks) {
+                int e = e4m3_block_exp(amax);
+                float inv = exp2_neg(e);
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) lo |= e4m3_encode(f[j] * inv) << (8 * j);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) hi |= e4m3_encode(f[4 + j] * inv) << (8 * j);
+                *reinterpret_cast<uint2*>(p.xq + i * 8) = make_uint2(lo, hi);
+                if ((i & 3) == 0) p.xsf[i >> 2] = (uint8_t)(e + 127);
+            }
+        }
+    }
+}
+
+// Routing and counting of one chunk of kRouteTokensPerBlock tokens.
+MOE_DEV void route_count_block(const RouteParams& p, int npl) {
     __shared__ int hist[kMaxExperts];
     __shared__ int base[kMaxExperts];
     __shared__ float sel_v[kRouteWaves][kMaxTopk];
@@ -121,9 +162,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_quant_kernel(RouteP
     if (p.logits) {
         for (int i = wave; i < ntok; i += kRouteWaves) {
             int64_t t = t0 + i;
-            route_token<NPL>(p.logits + t * p.E, p.E, k, p.score_fn, p.renorm,
-                             p.idx_out + t * k, p.w_out + t * k, sel_v[wave], sel_i[wave],
-                             pair_exp + i * k);
+            const float* lr = p.logits + t * p.E;
+            int32_t* io = p.idx_out + t * k;
+            float* wo = p.w_out + t * k;
+            if (npl <= 1) route_token<1>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], pair_exp + i * k);
+            else if (npl <= 2) route_token<2>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], pair_exp + i * k);
+            else if (npl <= 4) route_token<4>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], pair_exp + i * k);
+            else if (npl <= 8) route_token<8>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], pair_exp + i * k);
+            else route_token<16>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], pair_exp + i * k);
         }
     } else {
         for (int i = tid; i < ntok * k; i += kRouteThreads) {
@@ -154,38 +200,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_quant_kernel(RouteP
         p.slot_in_e[t0 * k + i] = pair_rank[i] >= 0 ? base[e] + pair_rank[i] : -1;
     }
 
-    // 3. activation quantisation: 4 lanes per 32-element group, 8 BF16 per lane
-    if (p.x) {
-        const int groups_per_row = p.H / kGroup;
-        const int tasks = ntok * groups_per_row * 4;
-        for (int i = tid; i < tasks; i += kRouteThreads) {
-            int q = i & 3;
-            int g = i >> 2;
-            int r = g / groups_per_row;
-            int gc = g - r * groups_per_row;
-            int64_t t = t0 + r;
-            const uint4 raw = *reinterpret_cast<const uint4*>(p.x + t * p.H + gc * kGroup + q * 8);
-            float f[8];
-            f[0] = bf16_to_f32(raw.x & 0xFFFFu); f[1] = bf16_to_f32(raw.x >> 16);
-            f[2] = bf16_to_f32(raw.y & 0xFFFFu); f[3] = bf16_to_f32(raw.y >> 16);
-            f[4] = bf16_to_f32(raw.z & 0xFFFFu); f[5] = bf16_to_f32(raw.z >> 16);
-            f[6] = bf16_to_f32(raw.w & 0xFFFFu); f[7] = bf16_to_f32(raw.w >> 16);
-            float amax = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf(f[j]));
-            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-            int e = e4m3_block_exp(amax);
-            float inv = exp2_neg(e);
-            uint32_t lo = 0, hi = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) lo |= e4m3_encode(f[j] * inv) << (8 * j);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) hi |= e4m3_encode(f[4 + j] * inv) << (8 * j);
-            *reinterpret_cast<uint2*>(p.xq + t * p.H + gc * kGroup + q * 8) = make_uint2(lo, hi);
-            if (q == 0) p.xsf[t * groups_per_row + gc] = (uint8_t)(e + 127);
-        }
-    }
+}
+
+// Blocks [0, ceil(T / kRouteTokensPerBlock)) route and count one chunk of
+// tokens each; every block then quantises its grid-stride share of x.
+__global__ __launch_bounds__(kRouteThreads) void route_count_quant_kernel(RouteParams p, int npl) {
+    if ((int64_t)blockIdx.x * kRouteTokensPerBlock < p.T) route_count_block(p, npl);
+    if (p.x) quant_rows(p);
 }
 
 // Exclusive scan of n <= 1024 ints in LDS by a 256-thread block: out[0..n].
@@ -270,19 +291,12 @@ __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p)
 
 hipError_t launch_route(const RouteParams& rp, const ScatterParams& sp, hipStream_t s) {
     if (rp.T > 0) {
-        dim3 grid((unsigned)((rp.T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock));
-        int npl = (rp.E + 63) / 64;
-        if (!rp.logits) npl = 1;
-        if (npl <= 1)
-            hipLaunchKernelGGL(route_count_quant_kernel<1>, grid, dim3(kRouteThreads), 0, s, rp);
-        else if (npl <= 2)
-            hipLaunchKernelGGL(route_count_quant_kernel<2>, grid, dim3(kRouteThreads), 0, s, rp);
-        else if (npl <= 4)
-            hipLaunchKernelGGL(route_count_quant_kernel<4>, grid, dim3(kRouteThreads), 0, s, rp);
-        else if (npl <= 8)
-            hipLaunchKernelGGL(route_count_quant_kernel<8>, grid, dim3(kRouteThreads), 0, s, rp);
-        else
-            hipLaunchKernelGGL(route_count_quant_kernel<16>, grid, dim3(kRouteThreads), 0, s, rp);
+        int64_t route_blocks = (rp.T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
+        int64_t quant_blocks = rp.x ? (rp.T * (rp.H / 8) + 4 * kRouteThreads - 1) / (4 * kRouteThreads) : 0;
+        dim3 grid((unsigned)std::min<int64_t>(std::max(route_blocks, std::min<int64_t>(quant_blocks, 2048)),
+                                              1 << 30));
+        const int npl = rp.logits ? (rp.E + 63) / 64 : 1;
+        hipLaunchKernelGGL(route_count_quant_kernel, grid, dim3(kRouteThreads), 0, s, rp, npl);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
