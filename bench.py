@@ -90,6 +90,7 @@ def setup_device(w, m, torch):
         for e, (b13, b2) in enumerate(ex.map(gen, range(w.E))):
             w13q[e], w13sf[e] = m.pack_weights(up(b13))
             w2q[e], w2sf[e] = m.pack_weights(up(b2))
+    w13sf, w2sf = m.scales_kmajor(w13sf, w.H), m.scales_kmajor(w2sf, w.I)
     torch.cuda.synchronize()
     return x, logits, w13q, w13sf, w2q, w2sf
 

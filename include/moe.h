@@ -80,9 +80,10 @@ typedef struct moe_dims {
  *   topk_idx  device, int32 [T, topk] expert ids (entries < 0 are skipped) and
  *   topk_w    device, float32 [T, topk] routing weights
  *   w13       device, FP4 [E, 2I, H/2]: rows [0, I) gate (W1), [I, 2I) up (W3)
- *   w13_sf    device, UE8M0 [E, 2I, H/32]
+ *   w13_sf    device, UE8M0 [E, H/128, 2I, 4]: K-step major (moe_scales_kmajor
+ *             of the per-row [E, 2I, H/32] scales)
  *   w2        device, FP4 [E, H, I/2]
- *   w2_sf     device, UE8M0 [E, H, I/32]
+ *   w2_sf     device, UE8M0 [E, I/128, H, 4]: K-step major
  *   y         device, BF16 [T, H], written
  *   ws        device workspace of at least moe_workspace_size() bytes,
  *             256-byte aligned, zeroed once by moe_workspace_init() after it is
@@ -118,8 +119,8 @@ typedef struct moe_args {
  *   offsets   int32 [E + 1]       exclusive prefix sum of counts
  *   slot_src  int32 [T*topk]      t*topk + j of position p (first offsets[E] valid)
  *   slot_of   int32 [T, topk]     position of pair (t, j), -1 when skipped
- *   xq, xsf   uint8 [T, H], [T, H/32]            quantised x
- *   hq, hsf   uint8 [T*topk, I], [T*topk, I/32]  quantised h by position
+ *   xq, xsf   uint8 [T, H], [H/128, T, 4]        quantised x (scales K-step major)
+ *   hq, hsf   uint8 [T*topk, I], [I/128, T*topk, 4]  quantised h by position
  *   o         BF16 [T*topk, H]                  GEMM2 rows by position */
 typedef struct moe_layout {
     size_t topk_idx, topk_w, counts, offsets, slot_src, slot_of;
@@ -172,6 +173,17 @@ int moe_quant_act(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* q, uin
  *   sf  device uint8 [rows, cols/32] out */
 int moe_pack_weights(const uint16_t* w, int64_t rows, int32_t cols, uint8_t* q, uint8_t* sf,
                      hipStream_t s);
+
+/* Weight-scale layout change for moe_forward (the layer's counterpart of a
+ * one-time weight transform): per-row scales [mats, rows, cols/32] become K-step
+ * major [mats, cols/128, rows, 4], so that the scales of many rows for one
+ * 128-wide K step are contiguous (one load per row block instead of one per
+ * row).
+ *   sf    device uint8 [mats, rows, cols/32] (e.g. from moe_pack_weights)
+ *   cols  K, a multiple of 128
+ *   out   device uint8 [mats, cols/128, rows, 4]; must not overlap sf */
+int moe_scales_kmajor(const uint8_t* sf, int64_t mats, int32_t rows, int32_t cols, uint8_t* out,
+                      hipStream_t s);
 
 /* The whole layer: route (or take topk_idx/topk_w), bucketise, quantise x,
  * GEMM1 + SwiGLU*weight -> FP8, GEMM2 -> BF16, combine into y. */

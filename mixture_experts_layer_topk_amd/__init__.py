@@ -52,13 +52,14 @@ class Layout(ctypes.Structure):
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_workspace_size", "moe_workspace_layout", "moe_workspace_init", "moe_route",
-           "moe_quant_act", "moe_pack_weights", "moe_forward", "moe_error_string")
+           "moe_quant_act", "moe_pack_weights", "moe_scales_kmajor", "moe_forward",
+           "moe_error_string")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
-                          "`python -m mixture_experts_layer_topk_amd.build`")
+                          "`python mixture_experts_layer_topk_amd/build.py`")
     lib = ctypes.CDLL(path)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     lib.moe_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(sz)]
@@ -67,6 +68,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_route.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_quant_act.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_pack_weights.argtypes = [vp, i64, i32, vp, vp, vp]
+    lib.moe_scales_kmajor.argtypes = [vp, i64, i32, i32, vp, vp]
     lib.moe_forward.argtypes = [ctypes.POINTER(Args), vp]
     lib.moe_error_string.argtypes = [ctypes.c_int]
     lib.moe_error_string.restype = ctypes.c_char_p
@@ -143,6 +145,23 @@ def pack_weights(w: torch.Tensor):
     return q, sf
 
 
+def scales_kmajor(sf: torch.Tensor, cols: int) -> torch.Tensor:
+    """Per-row scales [..., rows, cols/32] -> K-step major [..., cols/128, rows, 4]."""
+    rows = sf.shape[-2]
+    mats = sf.numel() // (rows * (cols // 32))
+    out = torch.empty(sf.shape[:-2] + (cols // 128, rows, 4), dtype=torch.uint8, device=sf.device)
+    _check(_lib.moe_scales_kmajor(_ptr(sf), mats, rows, cols, _ptr(out), _stream()))
+    return out
+
+
+def prepare_weights(w13: torch.Tensor, w2: torch.Tensor):
+    """BF16 expert weights W13 [E, 2I, H] and W2 [E, H, I] -> the four tensors
+    moe_forward takes (packed FP4 codes, K-step-major UE8M0 scales)."""
+    q13, s13 = pack_weights(w13)
+    q2, s2 = pack_weights(w2)
+    return q13, scales_kmajor(s13, w13.shape[-1]), q2, scales_kmajor(s2, w2.shape[-1])
+
+
 def route(d: Dims, logits: torch.Tensor, ws: torch.Tensor):
     """Top-k routing + bucketisation.  Returns a dict of device tensors."""
     T, k, E = d.T, d.topk, d.E
@@ -199,8 +218,9 @@ def intermediates(d: Dims, ws: torch.Tensor):
         slot_src=view(L.slot_src, R, torch.int32, (R,)),
         slot_of=view(L.slot_of, R, torch.int32, (T, k)),
         xq=view(L.xq, T * H, torch.uint8, (T, H)),
-        xsf=view(L.xsf, T * H // 32, torch.uint8, (T, H // 32)),
+        # scales are K-step major in the workspace; shown here per row
+        xsf=view(L.xsf, T * H // 32, torch.uint8, (H // 128, T, 4)).permute(1, 0, 2).reshape(T, H // 32),
         hq=view(L.hq, R * I, torch.uint8, (R, I)),
-        hsf=view(L.hsf, R * I // 32, torch.uint8, (R, I // 32)),
+        hsf=view(L.hsf, R * I // 32, torch.uint8, (I // 128, R, 4)).permute(1, 0, 2).reshape(R, I // 32),
         o=view(L.o, R * H, torch.int16, (R, H)),
     )

@@ -1,6 +1,7 @@
 """Build libmoe.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m mixture_experts_layer_topk_amd.build   (or build() from Python)
+Usage: python mixture_experts_layer_topk_amd/build.py  (run by path: importing the
+package loads the library this script builds)
 """
 from __future__ import annotations
 

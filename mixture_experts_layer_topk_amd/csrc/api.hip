@@ -170,6 +170,15 @@ int moe_pack_weights(const uint16_t* w, int64_t rows, int32_t cols, uint8_t* q, 
     return err == hipSuccess ? MOE_OK : hip_fail(err);
 }
 
+int moe_scales_kmajor(const uint8_t* sf, int64_t mats, int32_t rows, int32_t cols, uint8_t* out,
+                      hipStream_t s) {
+    if (mats < 0 || rows < 0 || cols <= 0 || cols % 128 != 0) return MOE_EINVAL;
+    if (mats == 0 || rows == 0) return MOE_OK;
+    if (!sf || !out || ((uintptr_t)sf & 3) || ((uintptr_t)out & 3) || sf == out) return MOE_EINVAL;
+    hipError_t err = moe::launch_scales_kmajor(sf, mats, rows, cols, out, s);
+    return err == hipSuccess ? MOE_OK : hip_fail(err);
+}
+
 int moe_forward(const moe_args_t* a, hipStream_t s) {
     if (!a) return MOE_EINVAL;
     const moe_dims_t& d = a->dims;

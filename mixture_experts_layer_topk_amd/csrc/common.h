@@ -58,25 +58,18 @@ MOE_DEV int e2m1_block_exp(float amax) { return block_exp<0x400000u, 2>(amax); }
 // 2^-e as a float for e in [-127, 127] (2^-127 is a float32 subnormal).
 MOE_DEV float exp2_neg(int e) { return __builtin_ldexpf(1.0f, -e); }
 
-// |x| <= 448 expected; larger magnitudes clamp to 448.  Nearest even.
-MOE_DEV uint32_t e4m3_encode(float x) {
-    uint32_t u = f2u(x);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t mag;
-    if (a >= 0x43E00000u) {                          // >= 448
-        mag = 0x7Eu;
-    } else if (a < 0x3C800000u) {                    // < 2^-6: subnormal grid m * 2^-9
-        mag = (uint32_t)__builtin_rintf(u2f(a) * 512.0f);   // exact scaling, RNE; 8 -> 2^-6
-    } else {
-        // rebias exponent 127 -> 7 and drop 20 mantissa bits, nearest even
-        uint32_t r = a - (120u << 23);
-        uint32_t q = r >> 20;
-        uint32_t rem = r & 0xFFFFFu;
-        q += (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u;
-        mag = q;
-    }
-    return sign | mag;
+// Two float32 values to E4M3 codes in the low 16 bits (first value in the low
+// byte), nearest even, by the gfx950 conversion instruction.  Inputs must be
+// finite with |x| <= 448 (the block scale guarantees it); on that range the
+// instruction rounds exactly as the format definition requires, which the
+// quantiser parity tests check code by code against the CPU reference.
+MOE_DEV uint32_t e4m3_pack2(float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+// Four values to one dword of E4M3 codes (first value in the low byte).
+MOE_DEV uint32_t e4m3_pack4(float a, float b, float c, float d) {
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
 }
 
 // |x| <= 6 expected; larger magnitudes clamp to 6.  Nearest, ties to the even

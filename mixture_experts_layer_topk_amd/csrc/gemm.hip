@@ -70,23 +70,28 @@ struct Cfg {
     static constexpr int kStages = 3;
     static constexpr int kAI = kABytes / 1024 / kWaves;   // 1 KiB load instructions per wave
     static constexpr int kBI = kBBytes / 1024 / kWaves;
-    static constexpr int kSAI = kSABytes / 256 / kWaves;  // 256-byte (dword per lane) loads
-    static constexpr int kSBI = kSBBytes / 256 / kWaves;
+    // scale tiles: one dword per lane, 64 rows per load; when a tile has fewer
+    // than 64 * kWaves rows the waves repeat each other's loads (same bytes to
+    // the same LDS address), so every wave issues the same number of loads
+    static constexpr int kSAI = (kSABytes + 256 * kWaves - 1) / (256 * kWaves);
+    static constexpr int kSBI = (kSBBytes + 256 * kWaves - 1) / (256 * kWaves);
+    static constexpr int kSARows = BM, kSBRows = BN;
     static constexpr int kLoads = kAI + kBI + kSAI + kSBI;  // per thread per stage
     static_assert(kABytes % (1024 * kWaves) == 0 && kBBytes % (1024 * kWaves) == 0, "tile / waves");
-    static_assert(kSABytes % (256 * kWaves) == 0 && kSBBytes % (256 * kWaves) == 0, "scales / waves");
+    static_assert(BM % 64 == 0 && BN % 64 == 0, "scale tiles in whole 64-row loads");
     static_assert(MT >= 1 && NT >= 2 && NT % 2 == 0, "wave tile");
     static_assert(kLoads < 64, "vmcnt range");
 };
 
-// LDS swizzles.  A fragment read touches 16 consecutive rows at one logical
-// 16-byte chunk; B the same for 16 consecutive rows of 64 bytes.  The XOR
-// patterns below put those 16 reads on distinct 16-byte bank slots both within
-// each 8-lane half (128-byte window) and across all 16 lanes (256-byte window).
-// Both depend on the row modulo 16 only, so the fragments of different m-tiles
-// (n-tiles) sit at constant offsets from one another.
-MOE_DEV int a_swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
-MOE_DEV int b_swz(int n) { return ((n >> 1) ^ ((n >> 3) & 1)) & 3; }
+// LDS swizzles.  An A fragment read touches 16 consecutive rows (128 bytes
+// each) at one logical 16-byte chunk; a B fragment read the same for rows of
+// 64 bytes.  The XOR patterns below were chosen by timing ds_read_b128 with
+// these exact lane patterns on gfx950: they run at the conflict-free rate
+// (the same as 64 consecutive 16-byte chunks), where the unswizzled layouts
+// take 2.3x as long.  Both depend on the row modulo 8 only, so the fragments
+// of different m-tiles (n-tiles) sit at constant offsets from one another.
+MOE_DEV int a_swz(int r) { return r & 7; }
+MOE_DEV int b_swz(int n) { return (n >> 1) & 3; }
 // A: row r, 16-byte chunk c (of 8) -> swizzled byte offset inside the A tile.
 MOE_DEV int a_off(int r, int c) { return r * BK + ((c ^ a_swz(r)) << 4); }
 // B: row n, 16-byte chunk c (of 4) -> swizzled byte offset inside the B tile.
@@ -98,7 +103,12 @@ MOE_DEV v4f mfma_fp8_fp4(const v8i& a, const v4i& b, const v4f& c, int sa, int s
                                                             sb);
 }
 
-MOE_DEV float silu(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + e^-g), with the hardware exp2 and reciprocal (about one
+// ulp each; a large negative g gives e^-g = inf and silu = -0).
+MOE_DEV float silu(float g) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
 // lgkmcnt[11:8], vmcnt[5:4] in bits [15:14]).
@@ -136,8 +146,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
 
     const int K = kG1 ? p.H : p.I;                 // reduction length
     const int nk = K / BK;
-    const int NTILES = kG1 ? (2 * p.I) / BN : (p.H + BN - 1) / BN;
-    const int sf_stride = K / kGroup;              // scale bytes per row
+    // n-tiles: GEMM1 covers BN/2 columns of I (gate and up), GEMM2 BN columns of H;
+    // the last one may be partial (I and H are multiples of 128)
+    const int NTILES = kG1 ? (p.I + BN / 2 - 1) / (BN / 2) : (p.H + BN - 1) / BN;
+    // Scales are stored K-step major: the 4 UE8M0 bytes of one 128-wide K step
+    // for row r sit at slab[ks][r][0..3], so a tile's scales for one K step are
+    // 4-byte entries of one slab rather than bytes strided across the rows.
+    const int64_t sa_slab = 4 * (kG1 ? p.T : p.T * p.topk);   // activation rows per slab
+    const int64_t sb_slab = 4 * (int64_t)(kG1 ? 2 * p.I : p.H); // weight rows per slab
     const uint8_t* a_base = kG1 ? p.xq : p.hq;
     const uint8_t* sa_base = kG1 ? p.xsf : p.hsf;
 
@@ -189,6 +205,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
             int nt = bl >> 4, c = bl & 15;
             if (kG1) {
                 int icol = ntile * (BN / 2) + ws * (C::WTN / 2) + c * (C::NT / 2) + (nt >> 1);
+                icol = min(icol, p.I - 1);          // partial last n-tile: never stored
                 return (nt & 1) ? p.I + icol : icol;
             } else {
                 int n = ntile * BN + ws * C::WTN + c * C::NT + nt;
@@ -198,8 +215,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
         const int64_t b_stride = K / 2;
         const uint8_t* w_base = kG1 ? p.w13 + (int64_t)e * (2 * p.I) * b_stride
                                     : p.w2 + (int64_t)e * p.H * b_stride;
-        const uint8_t* wsf_base = kG1 ? p.w13sf + (int64_t)e * (2 * p.I) * sf_stride
-                                      : p.w2sf + (int64_t)e * p.H * sf_stride;
+        const uint8_t* wsf_base = (kG1 ? p.w13sf : p.w2sf) + (int64_t)e * nk * sb_slab;
 
         // per-lane global sources of each load instruction (fixed over K), as
         // 32-bit byte offsets from wave-uniform bases
@@ -217,36 +233,49 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
             int c = (lane & 3) ^ b_swz(n);
             b_src[j] = (uint32_t)b_row(n) * (uint32_t)b_stride + c * 16;
         }
+        // 64-row block of scale load j of this wave (wrapping when the tile is short)
+        auto sa_blk = [&](int j) { return (j * C::kWaves + wave) % (C::kSARows / 64); };
+        auto sb_blk = [&](int j) { return (j * C::kWaves + wave) % (C::kSBRows / 64); };
         uint32_t sa_src[C::kSAI];
 #pragma unroll
-        for (int j = 0; j < C::kSAI; ++j)
-            sa_src[j] = (uint32_t)s_tok[64 * (j * C::kWaves + wave) + lane] * (uint32_t)sf_stride;
+        for (int j = 0; j < C::kSAI; ++j) sa_src[j] = (uint32_t)s_tok[64 * sa_blk(j) + lane] * 4u;
+        // B scales are staged in natural weight-row order: GEMM2 rows
+        // [ntile*BN, +BN); GEMM1 gate rows of I columns [ntile*BN/2, +BN/2), then
+        // the matching up rows.
+        auto sb_row = [&](int q) -> int {
+            if (kG1) {
+                int icol = min(ntile * (BN / 2) + (q % (BN / 2)), p.I - 1);
+                return q < BN / 2 ? icol : p.I + icol;
+            }
+            return min(ntile * BN + q, p.H - 1);
+        };
         uint32_t sb_src[C::kSBI];
 #pragma unroll
-        for (int j = 0; j < C::kSBI; ++j)
-            sb_src[j] = (uint32_t)b_row(64 * (j * C::kWaves + wave) + lane) * (uint32_t)sf_stride;
+        for (int j = 0; j < C::kSBI; ++j) sb_src[j] = (uint32_t)sb_row(64 * sb_blk(j) + lane) * 4u;
 
-        auto issue = [&](int ks, int stage) {   // K slice ks into LDS stage
+        // Load instruction j (of kLoads) of K slice ks into LDS stage `stage`:
+        // A tile chunks first, then B, then the two scale tiles.
+        auto issue_one = [&](int j, int ks, int stage) {
             uint8_t* sA = smem + stage * C::kStage;
             uint8_t* sB = sA + C::kABytes;
             uint8_t* sSA = sB + C::kBBytes;
             uint8_t* sSB = sSA + C::kSABytes;
-            const uint8_t* ga = a_base + ks * BK;
-            const uint8_t* gb = w_base + ks * (BK / 2);
-            const uint8_t* gsa = sa_base + ks * (BK / kGroup);
-            const uint8_t* gsb = wsf_base + ks * (BK / kGroup);
+            if (j < C::kAI) {
+                load_lds16(a_base + ks * BK + a_src[j], sA + (j * C::kWaves + wave) * 1024);
+            } else if (j < C::kAI + C::kBI) {
+                const int jb = j - C::kAI;
+                load_lds16(w_base + ks * (BK / 2) + b_src[jb], sB + (jb * C::kWaves + wave) * 1024);
+            } else if (j < C::kAI + C::kBI + C::kSAI) {
+                const int js = j - C::kAI - C::kBI;
+                load_lds4(sa_base + ks * sa_slab + sa_src[js], sSA + sa_blk(js) * 256);
+            } else {
+                const int js = j - C::kAI - C::kBI - C::kSAI;
+                load_lds4(wsf_base + ks * sb_slab + sb_src[js], sSB + sb_blk(js) * 256);
+            }
+        };
+        auto issue = [&](int ks, int stage) {   // K slice ks into LDS stage
 #pragma unroll
-            for (int j = 0; j < C::kAI; ++j)
-                load_lds16(ga + a_src[j], sA + (j * C::kWaves + wave) * 1024);
-#pragma unroll
-            for (int j = 0; j < C::kBI; ++j)
-                load_lds16(gb + b_src[j], sB + (j * C::kWaves + wave) * 1024);
-#pragma unroll
-            for (int j = 0; j < C::kSAI; ++j)
-                load_lds4(gsa + sa_src[j], sSA + (j * C::kWaves + wave) * 256);
-#pragma unroll
-            for (int j = 0; j < C::kSBI; ++j)
-                load_lds4(gsb + sb_src[j], sSB + (j * C::kWaves + wave) * 256);
+            for (int j = 0; j < C::kLoads; ++j) issue_one(j, ks, stage);
         };
 
         v4f acc[C::MT][C::NT];
@@ -262,7 +291,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
         const int a_lo = a_off(a_row0, lg), a_hi = a_off(a_row0, 4 + lg);
         const int b_fr = C::kABytes + b_off(b_row0, lg);
         const int sa_fr = C::kABytes + C::kBBytes + a_row0 * 4 + lg;
-        const int sb_fr = C::kABytes + C::kBBytes + C::kSABytes + b_row0 * 4 + lg;
+        // staged (natural-order) index of the B scale row behind LDS row b_row0 + nt*16:
+        // GEMM2 wn*WTN + l16*NT + nt; GEMM1 (nt odd: up half) + wn*WTN/2 + l16*NT/2 + nt/2
+        const int sb_fr = C::kABytes + C::kBBytes + C::kSABytes + lg +
+                          4 * (kG1 ? wn * (C::WTN / 2) + l16 * (C::NT / 2) : wn * C::WTN + l16 * C::NT);
+        auto sb_off = [&](int nt) { return 4 * (kG1 ? (nt & 1) * (BN / 2) + (nt >> 1) : nt); };
         constexpr int MH = C::MT / 2;
         static_assert(C::MT % 2 == 0 && MH <= C::NT, "A refill spread over the n-tiles");
         v8i a[C::MT];
@@ -277,7 +310,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
         };
         auto read_b = [&](const uint8_t* st, int nt) {
             b[nt] = *reinterpret_cast<const v4i*>(st + b_fr + nt * 16 * (BK / 2));
-            sb[nt] = st[sb_fr + nt * 64];
+            sb[nt] = st[sb_fr + sb_off(nt)];
         };
         auto mma = [&](int mt, int nt) {
             acc[mt][nt] = mfma_fp8_fp4(a[mt], b[nt], acc[mt][nt], sa[mt], sb[nt]);
@@ -311,12 +344,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
             __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));  // lgkmcnt(0)
             wait_vmcnt<C::kLoads>();
             barrier_nofence();
-            issue(min(ks + 3, nk - 1), (ks + 3) % C::kStages);
+            const int ks3 = min(ks + 3, nk - 1), st3 = (ks + 3) % C::kStages;
+            constexpr int LPG = (C::kLoads + C::NT - 1) / C::NT;   // loads issued per n-tile group
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int mt = MH; mt < C::MT; ++mt) mma(mt, nt);
+                for (int mt = MH; mt < C::MT; ++mt) {
+                    mma(mt, nt);
+                    // the loads of step ks + 3 ride between the MFMAs
+                    const int j = nt * LPG + (mt - MH);
+                    if (mt - MH < LPG && j < C::kLoads) issue_one(j, ks3, st3);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 read_b(nxt, nt);
                 if (nt < MH) read_a(nxt, nt);
@@ -365,21 +404,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
                     for (int o = 1; o < 32 / QN; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
                     const int ex = e4m3_block_exp(amax);
                     const float inv = exp2_neg(ex);
-                    if (r < valid) {
+                    const int col = icol0 + l16 * QN;
+                    if (r < valid && col < p.I) {
                         const int64_t pos = p0 + r;
-                        const int col = icol0 + l16 * QN;
                         uint8_t* dst = p.hq + pos * p.I + col;
-                        if constexpr (QN == 4) {
-                            uint32_t v = 0;
+                        static_assert(QN % 4 == 0, "whole dwords of E4M3 codes per lane");
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) v |= e4m3_encode(h[q] * inv) << (8 * q);
-                            *reinterpret_cast<uint32_t*>(dst) = v;
-                        } else {
-#pragma unroll
-                            for (int q = 0; q < QN; ++q) dst[q] = (uint8_t)e4m3_encode(h[q] * inv);
-                        }
+                        for (int q = 0; q < QN; q += 4)
+                            *reinterpret_cast<uint32_t*>(dst + q) =
+                                e4m3_pack4(h[q] * inv, h[q + 1] * inv, h[q + 2] * inv, h[q + 3] * inv);
                         if ((col & (kGroup - 1)) == 0)
-                            p.hsf[pos * (p.I / kGroup) + col / kGroup] = (uint8_t)(ex + 127);
+                            p.hsf[(int64_t)(col / (4 * kGroup)) * (p.T * p.topk) * 4 + pos * 4 +
+                                  (col / kGroup) % 4] = (uint8_t)(ex + 127);
                     }
                 }
             }
@@ -415,8 +451,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
     }
 }
 
-// Tile configuration: 256 x 256 output tiles, 4 waves of 128 x 128.
-constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 2;
+// Tile configuration: 128 x 512 output tiles, 4 waves of 128 x 128 side by
+// side.  128-row m-tiles waste fewer padding rows on ragged expert segments
+// than 256-row ones; the LDS and MFMA work per K step are those of 256 x 256.
+constexpr int kBM = 128, kBN = 512, kWM = 1, kWN = 4;
 
 int gemm_bm() { return kBM; }
 
@@ -437,7 +475,7 @@ static hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
         if (err != hipSuccess) return err;
         attr_set = true;
     }
-    const int ntiles = kG1 ? (2 * p.I) / kBN : (p.H + kBN - 1) / kBN;
+    const int ntiles = kG1 ? (p.I + kBN / 2 - 1) / (kBN / 2) : (p.H + kBN - 1) / kBN;
     const int64_t upper = (int64_t)p.max_mtiles * ntiles;
     const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(upper, cus));
     hipLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), lds, s, p);

@@ -20,7 +20,7 @@ struct RouteParams {
     int32_t* slot_in_e;         // [T, k] slot of the pair inside its expert
     const uint16_t* x;          // [T, H] BF16 or null (no quantisation)
     uint8_t* xq;                // [T, H]
-    uint8_t* xsf;               // [T, H/32]
+    uint8_t* xsf;               // [H/128, T, 4] (K-step major)
     int64_t T;
     int H, E, topk, score_fn, renorm;
 };
@@ -46,6 +46,8 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t rows, int cols, uint8_t* 
                             hipStream_t s);
 hipError_t launch_pack_weights(const uint16_t* w, int64_t rows, int cols, uint8_t* q,
                                uint8_t* sf, hipStream_t s);
+hipError_t launch_scales_kmajor(const uint8_t* sf, int64_t mats, int rows, int cols, uint8_t* out,
+                                hipStream_t s);
 
 // Grouped GEMMs.  Positions p index the per-expert segments produced by the
 // bucketisation: expert e owns p in [offsets[e], offsets[e+1]).
@@ -56,13 +58,13 @@ struct GemmParams {
     const int32_t* slot_src;    // [R] t*k + j of position p
     const float* topk_w;        // [T, k]
     const uint8_t* xq;          // [T, H]    GEMM1 A (gathered rows)
-    const uint8_t* xsf;         // [T, H/32]
+    const uint8_t* xsf;         // [H/128, T, 4]      K-step major scales
     const uint8_t* w13;         // [E, 2I, H/2]
-    const uint8_t* w13sf;       // [E, 2I, H/32]
+    const uint8_t* w13sf;       // [E, H/128, 2I, 4]
     uint8_t* hq;                // [R, I]    GEMM1 output / GEMM2 A
-    uint8_t* hsf;               // [R, I/32]
+    uint8_t* hsf;               // [I/128, R, 4]
     const uint8_t* w2;          // [E, H, I/2]
-    const uint8_t* w2sf;        // [E, H, I/32]
+    const uint8_t* w2sf;        // [E, I/128, H, 4]
     uint16_t* o;                // [R, H]    GEMM2 output (BF16)
     int64_t T;
     int H, I, E, topk;

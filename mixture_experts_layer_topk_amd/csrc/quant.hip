@@ -37,11 +37,8 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const uint16_t
         float amax = group_amax4(f);
         int e = e4m3_block_exp(amax);
         float inv = exp2_neg(e);
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) lo |= e4m3_encode(f[j] * inv) << (8 * j);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) hi |= e4m3_encode(f[4 + j] * inv) << (8 * j);
+        uint32_t lo = e4m3_pack4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+        uint32_t hi = e4m3_pack4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
         *reinterpret_cast<uint2*>(q + i * 8) = make_uint2(lo, hi);
         if ((i & 3) == 0) sf[i >> 2] = (uint8_t)(e + 127);
     }
@@ -63,6 +60,21 @@ __global__ __launch_bounds__(kQuantThreads) void pack_weights_kernel(const uint1
         for (int j = 0; j < 8; ++j) packed |= e2m1_encode(f[j] * inv) << (4 * j);
         reinterpret_cast<uint32_t*>(q)[i] = packed;
         if ((i & 3) == 0) sf[i >> 2] = (uint8_t)(e + 127);
+    }
+}
+
+// Per-row scales [mats][rows][cols/32] to K-step major [mats][cols/128][rows][4]:
+// thread i moves the 4 bytes of one (matrix, K step, row), rows fastest.
+__global__ __launch_bounds__(kQuantThreads) void scales_kmajor_kernel(const uint8_t* __restrict__ sf,
+                                                                      int64_t tasks, int rows,
+                                                                      int steps,
+                                                                      uint8_t* __restrict__ out) {
+    for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < tasks;
+         i += (int64_t)gridDim.x * kQuantThreads) {
+        const int64_t r = i % rows, ms = i / rows;
+        const int64_t step = ms % steps, mat = ms / steps;
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(sf + ((mat * rows + r) * steps + step) * 4);
+        reinterpret_cast<uint32_t*>(out)[i] = v;
     }
 }
 
@@ -89,4 +101,16 @@ hipError_t launch_pack_weights(const uint16_t* w, int64_t rows, int cols, uint8_
     return hipGetLastError();
 }
 
+}  // namespace moe
+
+namespace moe {
+hipError_t launch_scales_kmajor(const uint8_t* sf, int64_t mats, int rows, int cols, uint8_t* out,
+                                hipStream_t s) {
+    const int steps = cols / 128;
+    const int64_t tasks = mats * rows * (int64_t)steps;
+    if (tasks == 0) return hipSuccess;
+    hipLaunchKernelGGL(scales_kmajor_kernel, dim3(grid_for(tasks)), dim3(kQuantThreads), 0, s, sf,
+                       tasks, rows, steps, out);
+    return hipGetLastError();
+}
 }  // namespace moe

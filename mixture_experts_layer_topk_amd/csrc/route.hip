@@ -128,13 +128,15 @@ MOE_DEV void quant_rows(const RouteParams& p) {
             if (i < tasks) {
                 int e = e4m3_block_exp(amax);
                 float inv = exp2_neg(e);
-                uint32_t lo = 0, hi = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) lo |= e4m3_encode(f[j] * inv) << (8 * j);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) hi |= e4m3_encode(f[4 + j] * inv) << (8 * j);
+                uint32_t lo = e4m3_pack4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+                uint32_t hi = e4m3_pack4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
                 *reinterpret_cast<uint2*>(p.xq + i * 8) = make_uint2(lo, hi);
-                if ((i & 3) == 0) p.xsf[i >> 2] = (uint8_t)(e + 127);
+                if ((i & 3) == 0) {
+                    // scales K-step major: xsf[g / 4][t][g % 4] for group g of token t
+                    const int64_t G = i >> 2, gpr = p.H / kGroup;
+                    const int64_t t = G / gpr, g = G - t * gpr;
+                    p.xsf[(g >> 2) * (p.T * 4) + t * 4 + (g & 3)] = (uint8_t)(e + 127);
+                }
             }
         }
     }

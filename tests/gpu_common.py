@@ -95,16 +95,19 @@ class DeviceLayer:
                 self.w13q[e], self.w13sf[e] = q, s
                 q, s = m.pack_weights(bf16_dev(b2))
                 self.w2q[e], self.w2sf[e] = q, s
+        # per-row scales (compared with the oracle) and the K-step-major copies the layer takes
+        self.w13sf_k = m.scales_kmajor(self.w13sf, w.H)
+        self.w2sf_k = m.scales_kmajor(self.w2sf, w.I)
         self.d = m.dims(w.T, w.H, w.I, w.E, w.topk, w.score_fn, w.renorm)
         self.ws = m.new_workspace(self.d)
 
     def forward(self, use_logits=True):
         m = lib()
         if self.topk_idx is not None and not use_logits:
-            y = m.forward(self.d, self.x, self.w13q, self.w13sf, self.w2q, self.w2sf, self.ws,
+            y = m.forward(self.d, self.x, self.w13q, self.w13sf_k, self.w2q, self.w2sf_k, self.ws,
                           topk_idx=self.topk_idx, topk_w=self.topk_w)
         else:
-            y = m.forward(self.d, self.x, self.w13q, self.w13sf, self.w2q, self.w2sf, self.ws,
+            y = m.forward(self.d, self.x, self.w13q, self.w13sf_k, self.w2q, self.w2sf_k, self.ws,
                           logits=self.logits)
         torch.cuda.synchronize()
         return y

@@ -190,13 +190,21 @@ def test_forward_is_deterministic_and_workspace_reusable():
     # a smaller call on the same workspace, then the full call again
     m = G.lib()
     d_small = m.dims(100, w.H, w.I, w.E, w.topk)
-    y_small = m.forward(d_small, dl.x[:100], dl.w13q, dl.w13sf, dl.w2q, dl.w2sf, dl.ws,
+    y_small = m.forward(d_small, dl.x[:100], dl.w13q, dl.w13sf_k, dl.w2q, dl.w2sf_k, dl.ws,
                         logits=dl.logits[:100])
     torch.cuda.synchronize()
     ref_small = M.forward(dl.x_np[:100], *G.oracle_weights(w), topk=w.topk, I=w.I,
                           logits=dl.logits_np[:100])
     G.check_y(G.y_bits(y_small), ref_small["y"])
     assert np.array_equal(G.y_bits(dl.forward()), ys[0])
+
+
+def test_scales_kmajor_is_a_transpose():
+    _log("scales_kmajor")
+    rng = np.random.default_rng(5)
+    sf = rng.integers(0, 255, (3, 40, 7168 // 32), dtype=np.uint8)
+    out = G.lib().scales_kmajor(G.to_dev(sf), 7168).cpu().numpy()
+    assert np.array_equal(out, sf.reshape(3, 40, 7168 // 128, 4).transpose(0, 2, 1, 3))
 
 
 def test_forward_zero_tokens_is_noop():
