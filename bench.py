@@ -8,8 +8,11 @@ workload is the DeepSeek-V3-like one-GPU expert share (T=4096, H=7168,
 I=2048, E=32, top-8).  Prints one JSON line.
 
 Roofline: per-stage times come from HIP events the library records on the
-launch stream at stage boundaries inside the timed region; GEMM1 (two thirds of
-the FLOPs) is reported against the dense FP8-rate MFMA peak.  cpu_baseline: the
+launch stream at stage boundaries inside the timed region.  GEMM1 (two thirds of
+the FLOPs) is reported against the dense FP8-rate MFMA peak, or, for the decode
+workload, its algorithmic bytes against HBM bandwidth.  traffic is the HBM
+bytes per GEMM1 launch from the committed rocprofv3 counter summary, null when
+the kernel source has changed since the counters were taken.  cpu_baseline: the
 CPU oracle timed on a bounded sample of tokens of the same workload.
 """
 from __future__ import annotations
@@ -26,8 +29,12 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+METRIC = "MoE-layer tokens/s (FP8\u00d7FP4) at DSV3 shape; % scaled-MFMA peak / HBM GB/s"
 PEAK_MFMA_FP8_TFLOPS = 5000.0      # MI355X dense FP8-rate MFMA (FP8 x FP4 issues at this rate)
 PEAK_HBM_GBS = 8000.0
+# workloads whose GEMMs stream more weight bytes than they have FLOPs to hide
+HBM_BOUND = {"decode"}
+KERNEL_SOURCES = ("gemm.hip", "common.h", "kernels.h")
 
 
 def parse():
@@ -36,14 +43,17 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_prefill")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--cpu-sample-experts", type=int, default=1,
+                    help="experts whose rows the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before the timed steps, copy a buffer of this many MiB once (a "
                          "plain copy kernel of known size, to calibrate traffic counters)")
-    ap.add_argument("--flush-mb", type=int, default=0,
+    ap.add_argument("--flush-mb", type=int, default=None,
                     help="write this many MiB between steps (outside the timed events) to "
-                         "evict the last-level cache; 0 = off")
+                         "evict the 256 MB last-level cache; 0 = off; default 1024 for "
+                         "weight-streaming (decode) workloads, whose touched experts would "
+                         "otherwise stay cached, else 0")
     return ap.parse_args()
 
 
@@ -95,35 +105,112 @@ def setup_device(w, m, torch):
     return x, logits, w13q, w13sf, w2q, w2sf
 
 
-def cpu_baseline(w, ntok):
-    """The oracle on the first ntok tokens of the workload (routing of all T tokens
-    included); weight quantisation is input preparation and not timed."""
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_layer_topk_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def read_traffic(workload: str):
+    """HBM bytes per GEMM1 launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary of this workload, or None when there is none or the kernel source changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gemm1_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def gemm1_algorithmic_bytes(w, counts) -> float:
+    """Bytes GEMM1 must move at least: W1|W3 codes and scales of every expert that
+    receives a row, the quantised activations once, and the quantised h it writes."""
+    touched = int((counts > 0).sum())
+    w13 = 2 * w.I * (w.H // 2 + w.H // 32)
+    R = w.T * w.topk
+    return touched * w13 + w.T * (w.H + w.H // 32) + R * (w.I + w.I // 32)
+
+
+def roofline(w, counts, gemm1_ms):
+    kernel = "grouped_gemm_kernel<GEMM1> (FP8xFP4 MFMA + SwiGLU*w -> FP8)"
+    traffic = read_traffic(w.name)
+    alg_bytes = gemm1_algorithmic_bytes(w, counts)
+    if w.name in HBM_BOUND:
+        gbs = alg_bytes / (gemm1_ms * 1e-3) / 1e9
+        return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "alg_bytes": alg_bytes}
+    tflops = 4.0 * w.T * w.topk * w.I * w.H / (gemm1_ms * 1e-3) / 1e12
+    return {"kernel": kernel, "bound": "mfma", "achieved": round(tflops, 2),
+            "peak": PEAK_MFMA_FP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_MFMA_FP8_TFLOPS, 4), "traffic": traffic,
+            "alg_bytes": alg_bytes}
+
+
+def cpu_baseline(w, sample_experts: int):
+    """The oracle, timed on a bounded sample of the workload and scaled to tokens/s.
+
+    Timed in full: routing, bucketisation and activation quantisation of all T
+    tokens, and the combine of all T tokens.  Sampled: GEMM1 -> epilogue -> GEMM2
+    (the oracle's per-expert step) for every row of the first ``sample_experts``
+    experts that receive rows; its time is scaled by R / (rows sampled).  Only
+    the sampled experts' weights are generated and quantised (input preparation,
+    not timed)."""
     import moe_workloads as W
     from oracle import moe_ref as M
 
     x = W.gen_x(w)
     logits = W.gen_logits(w)
-    w13, w2 = W.gen_weights(w)
-    q13, s13 = M.pack_weights(w13)
-    q2, s2 = M.pack_weights(w2)
-    del w13, w2
-    toks = np.arange(min(ntok, w.T))
     t0 = time.perf_counter()
-    M.forward(x, q13, s13, q2, s2, topk=w.topk, I=w.I, logits=logits, score_fn=w.score_fn,
-              renorm=bool(w.renorm), tokens=toks)
-    dt = time.perf_counter() - t0
+    idx, wts = M.route(logits, w.topk, w.score_fn, bool(w.renorm))
+    counts, offsets, slot_src, slot_of = M.bucketize(idx, w.E)
+    xq, xsf = M.quant_act(x)
+    t_front = time.perf_counter() - t0
+
+    experts = [e for e in range(w.E) if counts[e] > 0][:sample_experts]
+    rows = 0
+    t_rows = 0.0
+    o = np.zeros((int(offsets[w.E]), w.H), np.uint16)
+    for e in experts:
+        q13, s13 = M.pack_weights(W.gen_expert_w13(w, e))
+        q2, s2 = M.pack_weights(W.gen_expert_w2(w, e))
+        pos = np.arange(offsets[e], offsets[e + 1])
+        f = slot_src[pos]
+        t, j = f // w.topk, f % w.topk
+        t0 = time.perf_counter()
+        _, _, _, o[pos] = M.expert_rows(xq[t], xsf[t], wts[t, j], q13, s13, q2, s2, w.I)
+        t_rows += time.perf_counter() - t0
+        rows += len(pos)
+    t0 = time.perf_counter()
+    M.combine(o, slot_of)
+    t_combine = time.perf_counter() - t0
+
+    R = int(offsets[w.E])
+    total = t_front + t_rows * R / rows + t_combine
     cores = len(os.sched_getaffinity(0))
-    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {len(toks)} of {w.T} tokens (routing, bucketisation and "
-                      f"quantisation over all {w.T}); {dt:.1f} s; numpy float64 BLAS on "
-                      f"{cores} host threads"}
+    return {"value": w.T / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"route+bucketise+quantise of all {w.T} tokens ({t_front:.1f} s) and "
+                      f"combine of all tokens ({t_combine:.1f} s) timed in full; the per-expert "
+                      f"GEMM1/epilogue/GEMM2 step timed on all {rows} rows of expert(s) "
+                      f"{experts} ({t_rows:.1f} s) and scaled by {R}/{rows} rows; numpy "
+                      f"float64 BLAS on {cores} host threads"}
 
 
 def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported "
-              "(the layer runs on one MI355X, see DESIGN.md for how it would shard)",
+              "(the layer runs on one MI355X; no multi-GPU path is built)",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -131,6 +218,8 @@ def main():
     import mixture_experts_layer_topk_amd as m
 
     w = W.WORKLOADS[a.workload]
+    if a.flush_mb is None:
+        a.flush_mb = 1024 if w.name in HBM_BOUND else 0
     x, logits, w13q, w13sf, w2q, w2sf = setup_device(w, m, torch)
     d = m.dims(w.T, w.H, w.I, w.E, w.topk, w.score_fn, w.renorm)
     ws = m.new_workspace(d)
@@ -174,12 +263,10 @@ def main():
     ms = float(np.mean(step_ms)) if flush is not None else wall * 1e3 / a.steps
     tokens_s = w.T / (ms * 1e-3)
 
-    R = w.T * w.topk
-    gemm1_flops = 4.0 * R * w.I * w.H
-    g1_tflops = gemm1_flops / (stage_ms[1] * 1e-3) / 1e12
+    counts = m.intermediates(d, ws)["counts"].cpu().numpy()
     layer_tflops = w.flops() / (ms * 1e-3) / 1e12
     out = {
-        "metric": "MoE-layer tokens/s (FP8xFP4) at DSV3 shape; % scaled-MFMA peak / HBM GB/s",
+        "metric": METRIC,
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -189,7 +276,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3 x fp4e2m1 (ue8m0/32) -> fp32 acc -> bf16",
+        "dtype": "fp8e4m3 x fp4e2m1 (ue8m0/32 scales), f32 accumulate",
         "data": "synthetic (seeded N(0,1) x and logits, N(0,0.02) BF16 weights quantised on the GPU)",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "topk": w.topk,
                    "score_fn": "sigmoid" if w.score_fn else "softmax", "renorm": bool(w.renorm),
@@ -197,13 +284,10 @@ def main():
         "layer_tflops": round(layer_tflops, 2),
         "layer_frac_mfma": round(layer_tflops / PEAK_MFMA_FP8_TFLOPS, 4),
         "stages_ms": {n: round(float(v), 4) for n, v in zip(m.STAGES, stage_ms)},
-        "roofline": {"kernel": "grouped_gemm_kernel<GEMM1> (FP8xFP4 MFMA + SwiGLU*w -> FP8)",
-                     "bound": "mfma", "achieved": round(g1_tflops, 2),
-                     "peak": PEAK_MFMA_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(g1_tflops / PEAK_MFMA_FP8_TFLOPS, 4), "traffic": None},
+        "roofline": roofline(w, counts, float(stage_ms[1])),
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_experts)
     print(json.dumps(out), flush=True)
 
 

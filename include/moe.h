@@ -58,7 +58,10 @@ extern "C" {
  *   E         experts, 1..1024
  *   topk      experts per token, 1..min(E, 16)
  *   score_fn  MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID (routing inside the library)
- *   renorm    nonzero: the k weights are divided by their sum */
+ *   renorm    nonzero: the k weights are divided by their sum
+ * T <= 2^24 and T*H, T*topk*I and H*I each below 2^32 (MOE_EUNSUPPORTED
+ * otherwise): the GEMMs address activation rows and one expert's weights with
+ * 32-bit byte offsets. */
 typedef struct moe_dims {
     int64_t T;
     int32_t H;

@@ -57,7 +57,11 @@ int check_dims(const moe_dims_t* d) {
     if (d->topk > d->E || d->topk > 16 || d->E > 1024) return MOE_EUNSUPPORTED;
     if (d->H % 128 != 0 || d->I % 128 != 0) return MOE_EUNSUPPORTED;
     if (d->score_fn != MOE_SCORE_SOFTMAX && d->score_fn != MOE_SCORE_SIGMOID) return MOE_EINVAL;
-    if ((int64_t)d->T * d->topk * (int64_t)d->H >= (1ll << 40)) return MOE_EUNSUPPORTED;
+    // the grouped GEMMs address A rows and one expert's weights with 32-bit byte offsets
+    const int64_t lim = 1ll << 32;
+    if ((int64_t)d->T * d->H >= lim || (int64_t)d->T * d->topk * d->I >= lim ||
+        (int64_t)d->H * d->I >= lim)
+        return MOE_EUNSUPPORTED;
     return MOE_OK;
 }
 

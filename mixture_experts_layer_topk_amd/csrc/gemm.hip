@@ -33,10 +33,16 @@
 // up rows) is read as is; the pages' offline 8-row gate/up interleave
 // ("原始权重布局") is replaced by this in-loader permutation.
 //
-// Tiles are handed out persistently: workgroup b takes tiles b, b + grid, ...
-// in (m-tile, n-tile) order, n fastest; an m-tile is BM consecutive positions
-// of one expert (the last one ragged), looked up in the per-m-tile expert
-// table the bucketisation writes.
+// Tiles are handed out persistently in a grouped order: tiles are numbered
+// in groups of kGM consecutive m-tiles x all n-tiles, m fastest inside a
+// group, and workgroup slot q takes tile numbers q, q + grid, ...  Workgroups
+// are dealt to the 8 XCDs round-robin (workgroup b runs on XCD b % 8), so
+// slots are assigned XCD-contiguously: the grid/8 workgroups of one XCD hold
+// consecutive slots, and in each round one XCD works on a rectangle of up to
+// kGM m-tiles by a few n-tiles, whose A rows and B columns are shared in its
+// own L2, instead of every XCD streaming every m-tile.  An m-tile is BM consecutive
+// positions of one expert (the last one ragged), looked up in the per-m-tile
+// expert table the bucketisation writes.
 //
 // Loads go straight from global memory to LDS (global_load_lds_dwordx4): one
 // instruction fills 1 KiB of LDS contiguously, lane l landing at byte 16 l, so
@@ -51,6 +57,8 @@
 namespace moe {
 
 constexpr int BK = 128;                 // K per MFMA step (bytes of FP8 A per row)
+constexpr int kGM = 8;                  // m-tiles per tile-order group
+constexpr int kXCDs = 8;                // XCDs of the chip, dealt workgroups round-robin
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -159,9 +167,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
 
     if (tid == 0) s_tile[3] = p.mtile_off[p.E];
     __syncthreads();
-    const int total = s_tile[3] * NTILES;
+    const int mtiles = s_tile[3];
+    const int total = mtiles * NTILES;
+    const int grid = gridDim.x;
+    const int slot = (grid % kXCDs) == 0
+                         ? (blockIdx.x % kXCDs) * (grid / kXCDs) + blockIdx.x / kXCDs
+                         : blockIdx.x;
 
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    for (int tile = slot; tile < total; tile += grid) {
         // Per-lane indices are re-derived from an opaque copy of the thread id in
         // every tile, so the compiler recomputes the (cheap) per-lane constants
         // here instead of keeping dozens of them alive across the K loop.
@@ -171,8 +184,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
         const int wave = tid_v >> 6;
         const int wm = wave / WN, wn = wave % WN;
         const int l16 = lane & 15, lg = lane >> 4;
-        const int mt_g = tile / NTILES;
-        const int ntile = tile - mt_g * NTILES;
+        const int grp = tile / (kGM * NTILES);
+        const int gm = min(kGM, mtiles - grp * kGM);      // m-tiles in this group
+        const int in_grp = tile - grp * (kGM * NTILES);
+        const int ntile = in_grp / gm;
+        const int mt_g = grp * kGM + (in_grp - ntile * gm);
         if (tid == 0) {
             const int e = p.mtile_e[mt_g];
             s_tile[0] = e;

@@ -39,7 +39,9 @@ def test_workspace_size_and_layout():
 
 @pytest.mark.parametrize("bad", [
     dict(H=100), dict(I=96), dict(topk=0), dict(topk=9, E=8), dict(E=0), dict(T=-1),
-    dict(score_fn=5), dict(E=2000), dict(topk=17, E=32)])
+    dict(score_fn=5), dict(E=2000), dict(topk=17, E=32),
+    # 32-bit GEMM offsets: T*H, T*topk*I and H*I must stay below 2^32
+    dict(T=1 << 19, H=8192), dict(T=1 << 18, topk=16, E=32, I=1024), dict(H=65536, I=65536)])
 def test_bad_dims_rejected(bad):
     m = _lib()
     args = dict(T=16, H=256, I=128, E=8, topk=2, score_fn=0)
