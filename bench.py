@@ -34,7 +34,8 @@ PEAK_MFMA_FP8_TFLOPS = 5000.0      # MI355X dense FP8-rate MFMA (FP8 x FP4 issue
 PEAK_HBM_GBS = 8000.0
 # workloads whose GEMMs stream more weight bytes than they have FLOPs to hide
 HBM_BOUND = {"decode"}
-KERNEL_SOURCES = ("gemm.hip", "common.h", "kernels.h")
+KERNEL_SOURCES = ("gemm.hip", "narrow.hip", "mfma.h", "common.h", "kernels.h")
+NARROW_ROWS_PER_EXPERT = 16        # moe_forward's choice between the two GEMM kernel families
 
 
 def parse():
@@ -50,10 +51,12 @@ def parse():
                     help="before the timed steps, copy a buffer of this many MiB once (a "
                          "plain copy kernel of known size, to calibrate traffic counters)")
     ap.add_argument("--flush-mb", type=int, default=None,
-                    help="write this many MiB between steps (outside the timed events) to "
+                    help="read this many MiB between steps (outside the timed events) to "
                          "evict the 256 MB last-level cache; 0 = off; default 1024 for "
                          "weight-streaming (decode) workloads, whose touched experts would "
-                         "otherwise stay cached, else 0")
+                         "otherwise stay cached, else 0.  A read leaves the cache clean, as "
+                         "the weight-reading kernels between two layers would; a write would "
+                         "leave it full of dirty lines whose write-backs slow the next reads")
     return ap.parse_args()
 
 
@@ -141,8 +144,14 @@ def gemm1_algorithmic_bytes(w, counts) -> float:
     return touched * w13 + w.T * (w.H + w.H // 32) + R * (w.I + w.I // 32)
 
 
+def gemm1_kernel_name(w) -> str:
+    if w.T * w.topk <= NARROW_ROWS_PER_EXPERT * w.E:
+        return "narrow_gemm_kernel<GEMM1> (weight-streaming FP8xFP4 MFMA + SwiGLU*w -> FP8)"
+    return "grouped_gemm_kernel<GEMM1> (tiled FP8xFP4 MFMA + SwiGLU*w -> FP8)"
+
+
 def roofline(w, counts, gemm1_ms):
-    kernel = "grouped_gemm_kernel<GEMM1> (FP8xFP4 MFMA + SwiGLU*w -> FP8)"
+    kernel = gemm1_kernel_name(w)
     traffic = read_traffic(w.name)
     alg_bytes = gemm1_algorithmic_bytes(w, counts)
     if w.name in HBM_BOUND:
@@ -224,7 +233,7 @@ def main():
     d = m.dims(w.T, w.H, w.I, w.E, w.topk, w.score_fn, w.renorm)
     ws = m.new_workspace(d)
     y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
-    flush = torch.empty(a.flush_mb << 20, dtype=torch.uint8, device="cuda") if a.flush_mb else None
+    flush = torch.ones(a.flush_mb << 18, dtype=torch.int32, device="cuda") if a.flush_mb else None
 
     hip = Hip()
     nstage = m.NUM_STAGE_EVENTS
@@ -248,7 +257,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(a.steps):
         if flush is not None:
-            flush.fill_(i & 0xFF)
+            flush.max()
         m.forward_raw(args_ev[i], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

@@ -72,8 +72,15 @@ typedef struct moe_dims {
     int32_t renorm;
 } moe_dims_t;
 
-/* Flags of moe_forward. */
+/* Flags of moe_forward.  The GEMMs run either as tiled kernels (128 x 512
+ * output tiles staged through LDS, for many rows per expert) or as narrow
+ * kernels (weights streamed from HBM straight into registers over many small
+ * workgroups, for few rows per expert, the decode regime).  By default
+ * moe_forward takes the narrow kernels when T * topk <= 16 * E.  Both give
+ * identical results; the flags force one (setting both is MOE_EINVAL). */
 #define MOE_FLAG_NONE 0u
+#define MOE_FLAG_NARROW 1u
+#define MOE_FLAG_TILED 2u
 
 #define MOE_NUM_STAGE_EVENTS 5
 

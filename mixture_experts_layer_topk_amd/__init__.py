@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
+FLAG_NONE, FLAG_NARROW, FLAG_TILED = 0, 1, 2
 
 
 class MoeError(RuntimeError):
@@ -192,11 +193,13 @@ def forward_raw(args: Args, stream=None):
 
 
 def forward(d: Dims, x, w13, w13_sf, w2, w2_sf, ws, logits=None, topk_idx=None, topk_w=None,
-            y=None):
-    """The whole layer; returns y (BF16 [T, H])."""
+            y=None, flags=FLAG_NONE):
+    """The whole layer; returns y (BF16 [T, H]).  flags: FLAG_NARROW / FLAG_TILED force
+    the GEMM kernel family (default: chosen from the rows per expert)."""
     if y is None:
         y = torch.empty((d.T, d.H), dtype=torch.bfloat16, device=x.device)
-    forward_raw(forward_args(d, x, w13, w13_sf, w2, w2_sf, y, ws, logits, topk_idx, topk_w))
+    forward_raw(forward_args(d, x, w13, w13_sf, w2, w2_sf, y, ws, logits, topk_idx, topk_w,
+                             flags=flags))
     return y
 
 

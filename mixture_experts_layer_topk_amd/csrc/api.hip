@@ -16,12 +16,28 @@ int hip_fail(hipError_t err) {
 }
 
 constexpr size_t kAlign = 256;
+// moe_forward picks the narrow GEMMs when T * topk <= this many rows per expert
+constexpr int64_t kNarrowRowsPerExpert = 16;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Carve {
-    size_t cnt, arrive, counts, offsets, mtile_off, mtile_e, topk_idx, topk_w, slot_in_e, slot_src, slot_of;
+    size_t cnt, arrive, counts, offsets, mtile_off, mtile_e, mtile_rec, sub_rec, nsub, topk_idx,
+        topk_w, slot_in_e, slot_src, slot_of;
     size_t xq, xsf, hq, hsf, o, total;
 };
+
+// Upper bound of the number of m-tiles: sum over experts of ceil(count / bm)
+// <= R / bm + (number of non-empty experts).
+int64_t max_mtiles(const moe_dims_t& d) {
+    const int64_t R = d.T * d.topk, bm = moe::gemm_bm();
+    return (R + bm - 1) / bm + std::min<int64_t>(d.E, R);
+}
+
+// The same bound for the 16-row sub-tiles of the narrow GEMMs.
+int64_t max_subs(const moe_dims_t& d) {
+    const int64_t R = d.T * d.topk;
+    return (R + moe::kSubRows - 1) / moe::kSubRows + std::min<int64_t>(d.E, R);
+}
 
 Carve carve(const moe_dims_t& d) {
     Carve c{};
@@ -33,7 +49,10 @@ Carve carve(const moe_dims_t& d) {
     c.counts = take(E * 4);
     c.offsets = take((E + 1) * 4);
     c.mtile_off = take((E + 1) * 4);
-    c.mtile_e = take(((R + moe::gemm_bm() - 1) / moe::gemm_bm() + std::min(E, R) + 1) * 4);
+    c.mtile_e = take((max_mtiles(d) + 1) * 4);
+    c.mtile_rec = take((max_mtiles(d) + 1) * 16);
+    c.sub_rec = take((max_subs(d) + 1) * 16);
+    c.nsub = take(4);
     c.topk_idx = take(R * 4);
     c.topk_w = take(R * 4);
     c.slot_in_e = take(R * 4);
@@ -152,6 +171,11 @@ int moe_route(const moe_dims_t* d, const float* logits, int32_t* topk_idx, float
     sp.E = d->E;
     sp.topk = d->topk;
     sp.bm = moe::gemm_bm();
+    sp.mtile_rec = at<int4>(ws, c.mtile_rec);
+    sp.max_mtiles = (int)max_mtiles(*d);
+    sp.sub_rec = at<int4>(ws, c.sub_rec);
+    sp.nsub = at<int32_t>(ws, c.nsub);
+    sp.max_subs = (int)max_subs(*d);
     hipError_t err = moe::launch_route(rp, sp, s);
     return err == hipSuccess ? MOE_OK : hip_fail(err);
 }
@@ -191,6 +215,9 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     if (d.T == 0) return MOE_OK;
     if (!a->x || !a->w13 || !a->w13_sf || !a->w2 || !a->w2_sf || !a->y || !a->ws) return MOE_EINVAL;
     if (!a->logits && (!a->topk_idx || !a->topk_w)) return MOE_EINVAL;
+    if ((a->flags & ~(MOE_FLAG_NARROW | MOE_FLAG_TILED)) ||
+        (a->flags & (MOE_FLAG_NARROW | MOE_FLAG_TILED)) == (MOE_FLAG_NARROW | MOE_FLAG_TILED))
+        return MOE_EINVAL;
     if (!aligned16(a->x) || !aligned16(a->w13) || !aligned16(a->w2) || !aligned16(a->y) ||
         ((uintptr_t)a->w13_sf & 3) || ((uintptr_t)a->w2_sf & 3))
         return MOE_EINVAL;
@@ -230,6 +257,11 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     sp.E = d.E;
     sp.topk = d.topk;
     sp.bm = moe::gemm_bm();
+    sp.mtile_rec = at<int4>(ws, c.mtile_rec);
+    sp.max_mtiles = (int)max_mtiles(d);
+    sp.sub_rec = at<int4>(ws, c.sub_rec);
+    sp.nsub = at<int32_t>(ws, c.nsub);
+    sp.max_subs = (int)max_subs(d);
     hipEvent_t* ev = a->stage_events;
     hipError_t err = ev ? hipEventRecord(ev[0], s) : hipSuccess;
     if (err == hipSuccess) err = moe::launch_route(rp, sp, s);
@@ -239,6 +271,9 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     gp.offsets = sp.offsets_out;
     gp.mtile_off = sp.mtile_off;
     gp.mtile_e = sp.mtile_e;
+    gp.mtile_rec = sp.mtile_rec;
+    gp.sub_rec = sp.sub_rec;
+    gp.nsub = sp.nsub;
     gp.slot_src = sp.slot_src;
     gp.topk_w = rp.w_out;
     gp.xq = rp.xq;
@@ -256,12 +291,16 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     gp.E = d.E;
     gp.topk = d.topk;
     const int64_t R = d.T * d.topk;
-    const int bm = moe::gemm_bm();
-    gp.max_mtiles = (int)((R + bm - 1) / bm + std::min<int64_t>(d.E, R));
+    gp.max_mtiles = (int)max_mtiles(d);
+    gp.max_subs = (int)max_subs(d);
+    // few rows per expert on average: the weight-streaming (narrow) kernels
+    bool narrow = R <= kNarrowRowsPerExpert * (int64_t)d.E;
+    if (a->flags & MOE_FLAG_NARROW) narrow = true;
+    if (a->flags & MOE_FLAG_TILED) narrow = false;
     if (ev) err = hipEventRecord(ev[1], s);
-    if (err == hipSuccess) err = moe::launch_gemm1(gp, s);
+    if (err == hipSuccess) err = narrow ? moe::launch_narrow_gemm1(gp, s) : moe::launch_gemm1(gp, s);
     if (err == hipSuccess && ev) err = hipEventRecord(ev[2], s);
-    if (err == hipSuccess) err = moe::launch_gemm2(gp, s);
+    if (err == hipSuccess) err = narrow ? moe::launch_narrow_gemm2(gp, s) : moe::launch_gemm2(gp, s);
     if (err == hipSuccess && ev) err = hipEventRecord(ev[3], s);
     if (err == hipSuccess) err = moe::launch_combine(gp.o, sp.slot_of, d.T, d.topk, d.H, a->y, s);
     if (err == hipSuccess && ev) err = hipEventRecord(ev[4], s);

@@ -53,10 +53,11 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "mfma.h"
 
 namespace moe {
 
-constexpr int BK = 128;                 // K per MFMA step (bytes of FP8 A per row)
+constexpr int BK = kKStep;              // K per MFMA step (bytes of FP8 A per row)
 constexpr int kGM = 8;                  // m-tiles per tile-order group
 constexpr int kXCDs = 8;                // XCDs of the chip, dealt workgroups round-robin
 
@@ -104,19 +105,6 @@ MOE_DEV int b_swz(int n) { return (n >> 1) & 3; }
 MOE_DEV int a_off(int r, int c) { return r * BK + ((c ^ a_swz(r)) << 4); }
 // B: row n, 16-byte chunk c (of 4) -> swizzled byte offset inside the B tile.
 MOE_DEV int b_off(int n, int c) { return n * (BK / 2) + ((c ^ b_swz(n)) << 4); }
-
-MOE_DEV v4f mfma_fp8_fp4(const v8i& a, const v4i& b, const v4f& c, int sa, int sb) {
-    v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b8, c, kFmtFp8, kFmtFp4, 0, sa, 0,
-                                                            sb);
-}
-
-// silu(g) = g / (1 + e^-g), with the hardware exp2 and reciprocal (about one
-// ulp each; a large negative g gives e^-g = inf and silu = -0).
-MOE_DEV float silu(float g) {
-    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
-    return g * __builtin_amdgcn_rcpf(1.0f + e);
-}
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
 // lgkmcnt[11:8], vmcnt[5:4] in bits [15:14]).
@@ -412,7 +400,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
 #pragma unroll
                     for (int q = 0; q < QN; ++q) {
                         float g = acc[mt][2 * q][i], u = acc[mt][2 * q + 1][i];
-                        h[q] = silu(g) * u * wr;
+                        h[q] = swiglu_w(g, u, wr);
                         amax = fmaxf(amax, __builtin_fabsf(h[q]));
                     }
                     // a 32-column group spans 32 / QN neighbouring lanes of the 16

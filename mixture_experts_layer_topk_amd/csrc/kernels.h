@@ -9,6 +9,7 @@
 namespace moe {
 
 constexpr int kRouteTokensPerBlock = 16;
+constexpr int kSubRows = 16;            // rows of a sub-tile (the narrow GEMMs' unit of rows)
 
 struct RouteParams {
     const float* logits;        // [T, E] or null
@@ -34,10 +35,14 @@ struct ScatterParams {
     int32_t* offsets_out;       // [E + 1]
     int32_t* mtile_off;         // [E + 1] prefix sum of ceil(count / bm)
     int32_t* mtile_e;           // [sum ceil(count / bm)] expert of each m-tile
+    int4* mtile_rec;            // [max_mtiles] {expert, first position, rows, 0}; rows = 0
+                                // past the last m-tile
+    int4* sub_rec;              // [max_subs] the same for 16-row sub-tiles
+    int32_t* nsub;              // [1] number of 16-row sub-tiles
     int32_t* slot_src;          // [T*k]
     int32_t* slot_of;           // [T, k]
     int64_t T;
-    int E, topk, bm;
+    int E, topk, bm, max_mtiles, max_subs;
 };
 
 hipError_t launch_route(const RouteParams& rp, const ScatterParams& sp, hipStream_t s);
@@ -55,6 +60,9 @@ struct GemmParams {
     const int32_t* offsets;     // [E + 1]
     const int32_t* mtile_off;   // [E + 1] m-tiles per expert, prefix-summed (tile rows = BM)
     const int32_t* mtile_e;     // [max_mtiles] expert of each m-tile
+    const int4* mtile_rec;      // [max_mtiles] {expert, first position, rows, 0}
+    const int4* sub_rec;        // [max_subs] the same for 16-row sub-tiles
+    const int32_t* nsub;        // [1] number of 16-row sub-tiles
     const int32_t* slot_src;    // [R] t*k + j of position p
     const float* topk_w;        // [T, k]
     const uint8_t* xq;          // [T, H]    GEMM1 A (gathered rows)
@@ -69,11 +77,16 @@ struct GemmParams {
     int64_t T;
     int H, I, E, topk;
     int max_mtiles;             // upper bound of mtile_off[E]
+    int max_subs;               // upper bound of *nsub
 };
 
 int gemm_bm();                  // rows per m-tile of the grouped GEMMs
 hipError_t launch_gemm1(const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm2(const GemmParams& p, hipStream_t s);
+// the same two GEMMs for few rows per expert (decode): N split over many small
+// workgroups that stream weights straight into registers
+hipError_t launch_narrow_gemm1(const GemmParams& p, hipStream_t s);
+hipError_t launch_narrow_gemm2(const GemmParams& p, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* o, const int32_t* slot_of, int64_t T, int topk, int H,
                           uint16_t* y, hipStream_t s);

@@ -1,0 +1,31 @@
+// Arithmetic shared by the two grouped-GEMM kernels (the tiled one for many
+// rows per expert and the narrow one for few).  Both feed every output element
+// through the same sequence of scaled MFMAs, one per 128-wide K step in
+// increasing K order, and the same epilogue, so the two give identical bits.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+constexpr int kKStep = 128;             // K per scaled MFMA (FP8 bytes of A per row)
+
+// One 16 x 16 x 128 block-scaled product: A FP8 E4M3 (32 bytes per lane), B FP4
+// E2M1 (16 bytes per lane), E8M0 scales in the low byte of sa / sb.
+MOE_DEV v4f mfma_fp8_fp4(const v8i& a, const v4i& b, const v4f& c, int sa, int sb) {
+    v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b8, c, kFmtFp8, kFmtFp4, 0, sa, 0,
+                                                            sb);
+}
+
+// silu(g) = g / (1 + e^-g), with the hardware exp2 and reciprocal (about one
+// ulp each; a large negative g gives e^-g = inf and silu = -0).
+MOE_DEV float silu(float g) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// GEMM1 epilogue value of one element: silu(gate) * up * routing weight.
+MOE_DEV float swiglu_w(float g, float u, float w) { return silu(g) * u * w; }
+
+}  // namespace moe

@@ -25,6 +25,7 @@ constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kMaxTopk = 16;
 constexpr int kMaxExperts = 1024;
+constexpr int kSmallPairs = 1024;       // T * k up to which one workgroup buckets every pair
 
 // (value, index) ordering of the top-k: larger value first, then smaller index.
 MOE_DEV bool better(float v, int i, float ov, int oi) {
@@ -142,25 +143,13 @@ MOE_DEV void quant_rows(const RouteParams& p) {
     }
 }
 
-// Routing and counting of one chunk of kRouteTokensPerBlock tokens.
-MOE_DEV void route_count_block(const RouteParams& p, int npl) {
-    __shared__ int hist[kMaxExperts];
-    __shared__ int base[kMaxExperts];
-    __shared__ float sel_v[kRouteWaves][kMaxTopk];
-    __shared__ int sel_i[kRouteWaves][kMaxTopk];
-    __shared__ int pair_rank[kRouteTokensPerBlock * kMaxTopk];
-    __shared__ int pair_exp[kRouteTokensPerBlock * kMaxTopk];   // expert of pair i of this block
-
+// Route tokens [t0, t0 + ntok) (one wave per token) or take the caller's ids;
+// pair i = (t - t0) * k + j of the chunk gets its expert in pair_exp[i].
+MOE_DEV void route_chunk(const RouteParams& p, int64_t t0, int ntok, int npl, int* pair_exp,
+                         float (*sel_v)[kMaxTopk], int (*sel_i)[kMaxTopk]) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int64_t t0 = (int64_t)blockIdx.x * kRouteTokensPerBlock;
-    const int ntok = (int)min<int64_t>(kRouteTokensPerBlock, p.T - t0);
     const int k = p.topk;
-
-    for (int e = tid; e < p.E; e += kRouteThreads) hist[e] = 0;
-
-    // 1. routing (one wave per token) or caller's ids
     if (p.logits) {
         for (int i = wave; i < ntok; i += kRouteWaves) {
             int64_t t = t0 + i;
@@ -183,6 +172,25 @@ MOE_DEV void route_count_block(const RouteParams& p, int npl) {
             }
         }
     }
+}
+
+// Routing and counting of one chunk of kRouteTokensPerBlock tokens.
+MOE_DEV void route_count_block(const RouteParams& p, int npl) {
+    __shared__ int hist[kMaxExperts];
+    __shared__ int base[kMaxExperts];
+    __shared__ float sel_v[kRouteWaves][kMaxTopk];
+    __shared__ int sel_i[kRouteWaves][kMaxTopk];
+    __shared__ int pair_rank[kRouteTokensPerBlock * kMaxTopk];
+    __shared__ int pair_exp[kRouteTokensPerBlock * kMaxTopk];   // expert of pair i of this block
+
+    const int tid = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * kRouteTokensPerBlock;
+    const int ntok = (int)min<int64_t>(kRouteTokensPerBlock, p.T - t0);
+    const int k = p.topk;
+
+    for (int e = tid; e < p.E; e += kRouteThreads) hist[e] = 0;
+    // 1. routing (one wave per token) or caller's ids
+    route_chunk(p, t0, ntok, npl, pair_exp, sel_v, sel_i);
     __syncthreads();
 
     // 2. count: LDS histogram; the LDS atomic's return is the pair's rank here
@@ -201,7 +209,6 @@ MOE_DEV void route_count_block(const RouteParams& p, int npl) {
         int e = pair_exp[i];
         p.slot_in_e[t0 * k + i] = pair_rank[i] >= 0 ? base[e] + pair_rank[i] : -1;
     }
-
 }
 
 // Blocks [0, ceil(T / kRouteTokensPerBlock)) route and count one chunk of
@@ -241,6 +248,47 @@ MOE_DEV void block_exclusive_scan(const int* in, int* out, int n, int* tmp) {
     __syncthreads();
 }
 
+// Per-expert tables of the GEMMs from the final counts cnt[E] and their
+// exclusive scan off[E + 1] (one workgroup): counts, offsets, then m-tiles of
+// p.bm rows (tiled GEMMs) and sub-tiles of kSubRows rows (narrow GEMMs): per
+// expert ceil(count / rows) tiles, prefix-summed, one record per tile
+// {expert, first position, rows}, zero records up to the table's size.
+MOE_DEV void write_tables(const ScatterParams& p, const int* cnt, const int* off, int* tiles,
+                          int* toff, int* tmp) {
+    const int tid = threadIdx.x;
+    for (int e = tid; e < p.E; e += kRouteThreads) p.counts_out[e] = cnt[e];
+    for (int e = tid; e <= p.E; e += kRouteThreads) p.offsets_out[e] = off[e];
+    for (int pass = 0; pass < 2; ++pass) {
+        const int rows = pass == 0 ? p.bm : kSubRows;
+        const int cap = pass == 0 ? p.max_mtiles : p.max_subs;
+        int4* rec = pass == 0 ? p.mtile_rec : p.sub_rec;
+        for (int e = tid; e < p.E; e += kRouteThreads) tiles[e] = ceil_div(cnt[e], rows);
+        __syncthreads();
+        block_exclusive_scan(tiles, toff, p.E, tmp);
+        const int ntiles = toff[p.E];
+        for (int m = tid; m < cap; m += kRouteThreads) {
+            int4 r = make_int4(0, 0, 0, 0);
+            if (m < ntiles) {
+                int lo = 0, hi = p.E - 1;          // expert e with toff[e] <= m < toff[e+1]
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (toff[mid] <= m) lo = mid; else hi = mid - 1;
+                }
+                const int r0 = (m - toff[lo]) * rows;
+                r = make_int4(lo, off[lo] + r0, min(rows, cnt[lo] - r0), 0);
+                if (pass == 0) p.mtile_e[m] = lo;
+            }
+            rec[m] = r;
+        }
+        if (pass == 0) {
+            for (int e = tid; e <= p.E; e += kRouteThreads) p.mtile_off[e] = toff[e];
+        } else if (tid == 0) {
+            *p.nsub = ntiles;
+        }
+        __syncthreads();                          // tiles and toff are reused
+    }
+}
+
 __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p) {
     __shared__ int cnt[kMaxExperts];
     __shared__ int off[kMaxExperts + 1];
@@ -263,19 +311,7 @@ __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p)
         for (int e = tid; e < p.E; e += kRouteThreads) p.cnt[e] = 0;
         if (tid == 0) *p.arrive = 0;
     }
-    if (blockIdx.x == 0) {
-        for (int e = tid; e < p.E; e += kRouteThreads) tiles[e] = ceil_div(cnt[e], p.bm);
-        __syncthreads();
-        block_exclusive_scan(tiles, toff, p.E, tmp);
-        for (int e = tid; e < p.E; e += kRouteThreads) {
-            p.counts_out[e] = cnt[e];
-            for (int m = toff[e]; m < toff[e + 1]; ++m) p.mtile_e[m] = e;
-        }
-        for (int e = tid; e <= p.E; e += kRouteThreads) {
-            p.offsets_out[e] = off[e];
-            p.mtile_off[e] = toff[e];
-        }
-    }
+    if (blockIdx.x == 0) write_tables(p, cnt, off, tiles, toff, tmp);
     const int64_t npairs = p.T * p.topk;
     for (int64_t i = (int64_t)blockIdx.x * kRouteThreads + tid; i < npairs;
          i += (int64_t)gridDim.x * kRouteThreads) {
@@ -291,7 +327,60 @@ __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p)
     }
 }
 
+
+// Few pairs (T * k <= kSmallPairs): workgroup 0 routes every token, counts the
+// pairs in an LDS histogram whose atomic returns each pair's rank inside its
+// expert, scans the counts, writes the tables and scatters the pairs, with no
+// global counters and no second launch ("05.10 Counting Sort /
+// Bucketization" 2.1-2.3 inside one workgroup).  Every workgroup quantises its
+// grid-stride share of x.
+__global__ __launch_bounds__(kRouteThreads) void route_small_kernel(RouteParams rp, ScatterParams sp,
+                                                                    int npl) {
+    if (blockIdx.x == 0) {
+        __shared__ int hist[kMaxExperts];
+        __shared__ int off[kMaxExperts + 1];
+        __shared__ int tiles[kMaxExperts];
+        __shared__ int toff[kMaxExperts + 1];
+        __shared__ int tmp[256];
+        __shared__ float sel_v[kRouteWaves][kMaxTopk];
+        __shared__ int sel_i[kRouteWaves][kMaxTopk];
+        __shared__ int pair_exp[kSmallPairs];
+        __shared__ int pair_rank[kSmallPairs];
+        const int tid = threadIdx.x;
+        const int k = rp.topk;
+        const int npairs = (int)rp.T * k;
+        for (int e = tid; e < rp.E; e += kRouteThreads) hist[e] = 0;
+        route_chunk(rp, 0, (int)rp.T, npl, pair_exp, sel_v, sel_i);
+        __syncthreads();
+        for (int i = tid; i < npairs; i += kRouteThreads) {
+            const int e = pair_exp[i];
+            pair_rank[i] = (e >= 0 && e < rp.E) ? atomicAdd(&hist[e], 1) : -1;
+        }
+        __syncthreads();
+        block_exclusive_scan(hist, off, rp.E, tmp);
+        for (int i = tid; i < npairs; i += kRouteThreads) {
+            const int e = pair_exp[i];
+            if (pair_rank[i] >= 0) {
+                const int pos = off[e] + pair_rank[i];
+                sp.slot_src[pos] = i;
+                sp.slot_of[i] = pos;
+            } else {
+                sp.slot_of[i] = -1;
+            }
+        }
+        write_tables(sp, hist, off, tiles, toff, tmp);
+    }
+    if (rp.x) quant_rows(rp);
+}
+
 hipError_t launch_route(const RouteParams& rp, const ScatterParams& sp, hipStream_t s) {
+    if (rp.T > 0 && rp.T * rp.topk <= kSmallPairs) {
+        int64_t quant_blocks = rp.x ? (rp.T * (rp.H / 8) + 4 * kRouteThreads - 1) / (4 * kRouteThreads) : 1;
+        dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(quant_blocks, 2048)));
+        const int npl = rp.logits ? (rp.E + 63) / 64 : 1;
+        hipLaunchKernelGGL(route_small_kernel, grid, dim3(kRouteThreads), 0, s, rp, sp, npl);
+        return hipGetLastError();
+    }
     if (rp.T > 0) {
         int64_t route_blocks = (rp.T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
         int64_t quant_blocks = rp.x ? (rp.T * (rp.H / 8) + 4 * kRouteThreads - 1) / (4 * kRouteThreads) : 0;

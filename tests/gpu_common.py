@@ -101,14 +101,14 @@ class DeviceLayer:
         self.d = m.dims(w.T, w.H, w.I, w.E, w.topk, w.score_fn, w.renorm)
         self.ws = m.new_workspace(self.d)
 
-    def forward(self, use_logits=True):
+    def forward(self, use_logits=True, flags=0):
         m = lib()
         if self.topk_idx is not None and not use_logits:
             y = m.forward(self.d, self.x, self.w13q, self.w13sf_k, self.w2q, self.w2sf_k, self.ws,
-                          topk_idx=self.topk_idx, topk_w=self.topk_w)
+                          topk_idx=self.topk_idx, topk_w=self.topk_w, flags=flags)
         else:
             y = m.forward(self.d, self.x, self.w13q, self.w13sf_k, self.w2q, self.w2sf_k, self.ws,
-                          logits=self.logits)
+                          logits=self.logits, flags=flags)
         torch.cuda.synchronize()
         return y
 

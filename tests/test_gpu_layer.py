@@ -82,9 +82,16 @@ def test_pack_weights_bit_exact(rows, cols):
 
 # ------------------------------------------------------------------ routing
 
-@pytest.mark.parametrize("name", list(W.WORKLOADS))
+# T * k = 1024 pairs is the largest case one workgroup buckets on its own; 1032 takes the
+# multi-workgroup path with global counters
+ROUTE_EDGES = {"pairs1024": W.Workload("pairs1024", T=128, H=256, I=128, E=32, topk=8),
+               "pairs1032": W.Workload("pairs1032", T=129, H=256, I=128, E=32, topk=8),
+               "e1024": W.Workload("e1024", T=3, H=128, I=128, E=1024, topk=16, score_fn=W.SIGMOID)}
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS) + list(ROUTE_EDGES))
 def test_route_bit_exact(name):
-    w = W.WORKLOADS[name]
+    w = W.WORKLOADS.get(name) or ROUTE_EDGES[name]
     _log(f"route {name}")
     m = G.lib()
     d = m.dims(w.T, w.H, w.I, w.E, w.topk, w.score_fn, w.renorm)
@@ -197,6 +204,37 @@ def test_forward_is_deterministic_and_workspace_reusable():
                           logits=dl.logits_np[:100])
     G.check_y(G.y_bits(y_small), ref_small["y"])
     assert np.array_equal(G.y_bits(dl.forward()), ys[0])
+
+
+# few rows per expert (decode), more than 16 rows per expert (several 16-row passes of the
+# narrow kernels), K-step counts below and not a multiple of the narrow kernels' four-way
+# K split, and all rows on one expert
+AGREE_SHAPES = [W.WORKLOADS["decode"], W.WORKLOADS["tiny"], RAGGED,
+                W.Workload("mid", T=96, H=2048, I=512, E=32, topk=8),
+                W.Workload("hot1", T=300, H=256, I=128, E=8, topk=1)]
+
+
+@pytest.mark.parametrize("w", AGREE_SHAPES, ids=lambda w: w.name)
+def test_narrow_and_tiled_gemms_match_oracle(w):
+    """Both GEMM kernel families, forced on the same inputs, against the oracle (the
+    default picks one family per shape; this runs the other one too)."""
+    m = G.lib()
+    _log(f"narrow and tiled {w.name}")
+    ext = None
+    if w.name == "hot1":
+        ext = (np.full((w.T, 1), 3, np.int32), np.ones((w.T, 1), np.float32))
+    dl = G.DeviceLayer(w, external_topk=ext)
+    ref = _oracle_full(w, ext)
+    so_r = ref["slot_of"].reshape(-1)
+    for name, flag in (("narrow", m.FLAG_NARROW), ("tiled", m.FLAG_TILED)):
+        _log(f"  {name}")
+        y = dl.forward(use_logits=ext is None, flags=flag)
+        inter = dl.intermediates()
+        so_g = inter["slot_of"].reshape(-1)
+        ok = so_r >= 0
+        G.check_hq(inter["hq"][so_g[ok]], inter["hsf"][so_g[ok]], ref["hq"][so_r[ok]],
+                   ref["hsf"][so_r[ok]])
+        G.check_y(G.y_bits(y), ref["y"])
 
 
 def test_scales_kmajor_is_a_transpose():

@@ -70,6 +70,10 @@ def test_forward_rejects_null_and_small_workspace_without_gpu():
     a.x = ctypes.c_void_p((1 << 20) + 2)                                       # misaligned x
     a.ws = ctypes.c_void_p(1 << 20)
     assert m._lib.moe_forward(ctypes.byref(a), None) == m.MOE_EINVAL
+    a.x = fake
+    for bad_flags in (m.FLAG_NARROW | m.FLAG_TILED, 4, 1 << 31):               # unknown or both
+        a.flags = bad_flags
+        assert m._lib.moe_forward(ctypes.byref(a), None) == m.MOE_EINVAL
 
 
 def test_quant_and_pack_reject_bad_sizes():
