@@ -123,6 +123,15 @@ MOE_DEV void barrier_nofence() {
     asm volatile("" ::: "memory");
 }
 
+// Scale tiles are staged so that one lane's scales of four consecutive
+// 16-row (16-column) MFMA tiles are one 16-byte run: inside every group of 64
+// staged dwords, slot q holds the scales of tile row
+//   (q & ~63) | (q & 3) << 4 | (q >> 2) & 15,
+// i.e. row 16 t + r of tile t < 4 sits at slot 4 r + t.  A lane (row r)
+// then reads tiles 4h .. 4h + 3 with one ds_read_b128 at slot 64 h + 4 r, and
+// the 16 lanes of one lane group read 256 consecutive bytes (no conflicts).
+MOE_DEV int scale_slot_row(int q) { return (q & ~63) | ((q & 3) << 4) | ((q >> 2) & 15); }
+
 MOE_DEV void load_lds16(const void* g, uint8_t* lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
 }
@@ -242,20 +251,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
         auto sb_blk = [&](int j) { return (j * C::kWaves + wave) % (C::kSBRows / 64); };
         uint32_t sa_src[C::kSAI];
 #pragma unroll
-        for (int j = 0; j < C::kSAI; ++j) sa_src[j] = (uint32_t)s_tok[64 * sa_blk(j) + lane] * 4u;
-        // B scales are staged in natural weight-row order: GEMM2 rows
-        // [ntile*BN, +BN); GEMM1 gate rows of I columns [ntile*BN/2, +BN/2), then
-        // the matching up rows.
-        auto sb_row = [&](int q) -> int {
-            if (kG1) {
-                int icol = min(ntile * (BN / 2) + (q % (BN / 2)), p.I - 1);
-                return q < BN / 2 ? icol : p.I + icol;
-            }
-            return min(ntile * BN + q, p.H - 1);
-        };
+        for (int j = 0; j < C::kSAI; ++j)
+            sa_src[j] = (uint32_t)s_tok[scale_slot_row(64 * sa_blk(j) + lane)] * 4u;
+        // B scales are staged in the B tile's LDS row order, regrouped by
+        // scale_slot_row: the slots of LDS row q hold weight row b_row(q).
         uint32_t sb_src[C::kSBI];
 #pragma unroll
-        for (int j = 0; j < C::kSBI; ++j) sb_src[j] = (uint32_t)sb_row(64 * sb_blk(j) + lane) * 4u;
+        for (int j = 0; j < C::kSBI; ++j)
+            sb_src[j] = (uint32_t)b_row(scale_slot_row(64 * sb_blk(j) + lane)) * 4u;
 
         // Load instruction j (of kLoads) of K slice ks into LDS stage `stage`:
         // A tile chunks first, then B, then the two scale tiles.
@@ -294,14 +297,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
         const int b_row0 = wn * C::WTN + l16;
         const int a_lo = a_off(a_row0, lg), a_hi = a_off(a_row0, 4 + lg);
         const int b_fr = C::kABytes + b_off(b_row0, lg);
-        const int sa_fr = C::kABytes + C::kBBytes + a_row0 * 4 + lg;
-        // staged (natural-order) index of the B scale row behind LDS row b_row0 + nt*16:
-        // GEMM2 wn*WTN + l16*NT + nt; GEMM1 (nt odd: up half) + wn*WTN/2 + l16*NT/2 + nt/2
-        const int sb_fr = C::kABytes + C::kBBytes + C::kSABytes + lg +
-                          4 * (kG1 ? wn * (C::WTN / 2) + l16 * (C::NT / 2) : wn * C::WTN + l16 * C::NT);
-        auto sb_off = [&](int nt) { return 4 * (kG1 ? (nt & 1) * (BN / 2) + (nt >> 1) : nt); };
-        constexpr int MH = C::MT / 2;
-        static_assert(C::MT % 2 == 0 && MH <= C::NT, "A refill spread over the n-tiles");
+        // scale runs of this lane: tiles 4h .. 4h+3 at slot base + 64 h + 4 l16
+        const int sa_fr = C::kABytes + C::kBBytes + 4 * (wm * C::WTM + 4 * l16);
+        const int sb_fr = C::kABytes + C::kBBytes + C::kSABytes + 4 * (wn * C::WTN + 4 * l16);
+        static_assert(C::MT % 4 == 0 && C::NT % 4 == 0, "scale runs of four tiles");
         v8i a[C::MT];
         int sa[C::MT];
         v4i b[C::NT];
@@ -310,74 +309,62 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
             v4i lo = *reinterpret_cast<const v4i*>(st + a_lo + mt * 16 * BK);
             v4i hi = *reinterpret_cast<const v4i*>(st + a_hi + mt * 16 * BK);
             a[mt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            sa[mt] = st[sa_fr + mt * 64];
         };
         auto read_b = [&](const uint8_t* st, int nt) {
             b[nt] = *reinterpret_cast<const v4i*>(st + b_fr + nt * 16 * (BK / 2));
-            sb[nt] = st[sb_fr + sb_off(nt)];
+        };
+        // lane group lg supplies the scale of K group lg: byte lg of each dword
+        auto read_scales = [&](const uint8_t* st) {
+#pragma unroll
+            for (int h = 0; h < C::MT / 4; ++h) {
+                const v4i v = *reinterpret_cast<const v4i*>(st + sa_fr + 256 * h);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) sa[4 * h + t] = (int)((uint32_t)v[t] >> (8 * lg));
+            }
+#pragma unroll
+            for (int h = 0; h < C::NT / 4; ++h) {
+                const v4i v = *reinterpret_cast<const v4i*>(st + sb_fr + 256 * h);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) sb[4 * h + t] = (int)((uint32_t)v[t] >> (8 * lg));
+            }
         };
         auto mma = [&](int mt, int nt) {
             acc[mt][nt] = mfma_fp8_fp4(a[mt], b[nt], acc[mt][nt], sa[mt], sb[nt]);
         };
 
-        // One K step, in two halves, every operand register refilled right after
-        // its last use.  On entry the registers hold step ks's B fragments and
-        // the A fragments of m-tiles [0, MT/2).
-        //  first half  m-tiles [0, MT/2), m-major; meanwhile A of m-tiles
-        //              [MT/2, MT) of step ks is read from stage ks;
-        //  barrier     stage ks is fully in registers and is retired; stage
-        //              ks + 1 is published; the loads of step ks + 3 go into the
-        //              retired stage (the last steps reload the final K slice,
-        //              which the L2 still holds, so the body has no branches);
-        //  second half m-tiles [MT/2, MT), n-major; B of n-tile nt and A of
-        //              m-tile nt < MT/2 of step ks + 1 are read from stage ks + 1
-        //              as soon as n-tile nt is done.  On the last step these
-        //              reads fetch a stage nobody uses.
-        auto step = [&](int ks) {
+        // Two waves per SIMD (8 waves): the SIMD's other wave runs its MFMAs
+        // while this one waits on LDS, the barrier or the load queue, so one
+        // K step is simply: read step ks's A fragments, then per n-tile its B
+        // fragment, its four MFMAs and one load of step ks + 2 into the stage
+        // every wave has retired (spreading the load issue between the MFMAs
+        // measured 5% faster than issuing them all first), then wait for this
+        // wave's loads of step ks + 1 and barrier.
+        auto step8 = [&](int ks) {
             const uint8_t* cur = smem + (ks % C::kStages) * C::kStage;
-            const uint8_t* nxt = smem + ((ks + 1) % C::kStages) * C::kStage;
+            const int ks2 = min(ks + 2, nk - 1), st2 = (ks + 2) % C::kStages;
+            read_scales(cur);
 #pragma unroll
-            for (int mt = 0; mt < MH; ++mt) {
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int nt = 0; nt < C::NT; ++nt) mma(mt, nt);
-                __builtin_amdgcn_sched_barrier(0);
-                read_a(cur, MH + mt);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));  // lgkmcnt(0)
-            wait_vmcnt<C::kLoads>();
-            barrier_nofence();
-            const int ks3 = min(ks + 3, nk - 1), st3 = (ks + 3) % C::kStages;
-            constexpr int LPG = (C::kLoads + C::NT - 1) / C::NT;   // loads issued per n-tile group
+            for (int mt = 0; mt < C::MT; ++mt) read_a(cur, mt);
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt) {
+                read_b(cur, nt);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int mt = MH; mt < C::MT; ++mt) {
-                    mma(mt, nt);
-                    // the loads of step ks + 3 ride between the MFMAs
-                    const int j = nt * LPG + (mt - MH);
-                    if (mt - MH < LPG && j < C::kLoads) issue_one(j, ks3, st3);
-                }
+                for (int mt = 0; mt < C::MT; ++mt) mma(mt, nt);
+                if (nt < C::kLoads) issue_one(nt, ks2, st2);
                 __builtin_amdgcn_sched_barrier(0);
-                read_b(nxt, nt);
-                if (nt < MH) read_a(nxt, nt);
             }
-            __builtin_amdgcn_sched_barrier(0);
+            static_assert(C::kLoads <= C::NT, "one load per n-tile group");
+            wait_vmcnt<C::kLoads>();
+            barrier_nofence();
         };
-
+        static_assert(C::kWaves == 8, "the K-step schedule assumes two waves per SIMD");
         wait_vmcnt<0>();
         issue(0, 0);
         issue(min(1, nk - 1), 1);
-        issue(min(2, nk - 1), 2);
-        wait_vmcnt<2 * C::kLoads>();
+        wait_vmcnt<C::kLoads>();
         barrier_nofence();
-#pragma unroll
-        for (int mt = 0; mt < MH; ++mt) read_a(smem, mt);
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) read_b(smem, nt);
-        for (int ks = 0; ks < nk; ++ks) step(ks);
+        for (int ks = 0; ks < nk; ++ks) step8(ks);
         wait_vmcnt<0>();
         __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));  // lgkmcnt(0)
 
@@ -458,7 +445,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
 // Tile configuration: 128 x 512 output tiles, 4 waves of 128 x 128 side by
 // side.  128-row m-tiles waste fewer padding rows on ragged expert segments
 // than 256-row ones; the LDS and MFMA work per K step are those of 256 x 256.
-constexpr int kBM = 128, kBN = 512, kWM = 1, kWN = 4;
+constexpr int kBM = 128, kBN = 512, kWM = 2, kWN = 4;
 
 int gemm_bm() { return kBM; }
 

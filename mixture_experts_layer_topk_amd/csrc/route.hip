@@ -16,6 +16,8 @@
 //   offsets and writes t*k + j to position offsets[e] + slot (2.3 SCATTER) and
 //   the inverse map.  The last workgroup to finish zeroes the global counters,
 //   so the workspace is ready for the next call without a host memset.
+#include <rocprim/block/block_scan.hpp>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -27,51 +29,75 @@ constexpr int kMaxTopk = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kSmallPairs = 1024;       // T * k up to which one workgroup buckets every pair
 
-// (value, index) ordering of the top-k: larger value first, then smaller index.
-MOE_DEV bool better(float v, int i, float ov, int oi) {
-    return v > ov || (v == ov && i < oi);
+// Unsigned integer with the order of the float value (finite inputs); -0 and
+// +0 map to the same integer, as they compare equal.
+MOE_DEV uint32_t float_order(float v) {
+    const uint32_t u = f2u(v == 0.0f ? 0.0f : v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // Top-k of one token's E logits with one wave.  Lane l owns experts
 // l, l + 64, ...; NPL = values per lane.  Writes idx/w for the token.
+//
+// Every expert gets a unique 42-bit key, its float order in the high bits and
+// 1023 - e in the low 10, so a larger key means a larger logit, or an equal
+// logit and a smaller index (the tie rule).  The k-th largest key T is found
+// bit by bit from the top: a candidate bit is kept when at least k keys are
+// >= the candidate, each count a ballot and a popcount per value slot (no LDS
+// traffic).  The k keys >= T are then compacted into LDS and each is ranked
+// by the number of selected keys above it, which orders the slots.
 template <int NPL>
 MOE_DEV void route_token(const float* __restrict__ lrow, int E, int k, int score_fn, int renorm,
                          int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-                         float* sel_v, int* sel_i, int* lds_idx) {
+                         float* sel_v, int* sel_i, uint64_t* sel_k, int* lds_idx) {
     const int lane = threadIdx.x & 63;
     float v[NPL];
-    uint32_t taken = 0;
+    uint64_t key[NPL];
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
-        int e = lane + 64 * i;
+        const int e = lane + 64 * i;
         v[i] = e < E ? lrow[e] : 0.0f;
-        if (e >= E) taken |= 1u << i;
+        key[i] = e < E ? ((uint64_t)float_order(v[i]) << 10) | (uint64_t)(1023 - e) : 0;
     }
-    for (int r = 0; r < k; ++r) {
-        float bv = 0.0f;
-        int bi = 0x7FFFFFFF;
+    uint64_t T = 0;
+    for (int bit = 41; bit >= 0; --bit) {
+        const uint64_t c = T | (1ull << bit);
+        int cnt = 0;
 #pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-            bool free_ = !((taken >> i) & 1u);
-            if (free_ && (bi == 0x7FFFFFFF || better(v[i], lane + 64 * i, bv, bi))) {
-                bv = v[i];
-                bi = lane + 64 * i;
-            }
-        }
+        for (int i = 0; i < NPL; ++i) cnt += __popcll(__ballot(key[i] >= c));
+        if (cnt >= k) T = c;
+    }
+    // compact the k selected keys (and their logits) into LDS
+    int base = 0;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            float ov = __shfl_xor(bv, o, 64);
-            int oi = __shfl_xor(bi, o, 64);
-            if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi))) {
-                bv = ov;
-                bi = oi;
-            }
+    for (int i = 0; i < NPL; ++i) {
+        const bool sel = key[i] >= T;
+        const uint64_t m = __ballot(sel);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (sel) {
+            sel_k[base + below] = key[i];
+            sel_v[base + below] = v[i];
         }
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        if (lane == 0) {
-            sel_v[r] = bv;
-            sel_i[r] = bi;
-        }
+        base += __popcll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint64_t x = 0;
+    float xv = 0.0f;
+    int rank = 0;
+    if (lane < k) {
+        x = sel_k[lane];
+        xv = sel_v[lane];
+        for (int j = 0; j < k; ++j) rank += sel_k[j] > x;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < k) {
+        sel_v[rank] = xv;
+        sel_i[rank] = 1023 - (int)(x & 1023);
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -101,11 +127,11 @@ MOE_DEV void route_token(const float* __restrict__ lrow, int E, int k, int score
 }
 
 // Quantise x rows [T, H]: task i covers 8 elements of the flattened array.
-MOE_DEV void quant_rows(const RouteParams& p) {
+MOE_DEV void quant_rows(const RouteParams& p, int block, int nblocks) {
     const int64_t tasks = p.T * (p.H / 8);
-    const int64_t stride = (int64_t)gridDim.x * kRouteThreads;
+    const int64_t stride = (int64_t)nblocks * kRouteThreads;
     constexpr int U = 4;
-    for (int64_t i0 = (int64_t)blockIdx.x * kRouteThreads + threadIdx.x; i0 < tasks; i0 += U * stride) {
+    for (int64_t i0 = (int64_t)block * kRouteThreads + threadIdx.x; i0 < tasks; i0 += U * stride) {
         uint4 raw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -146,7 +172,8 @@ MOE_DEV void quant_rows(const RouteParams& p) {
 // Route tokens [t0, t0 + ntok) (one wave per token) or take the caller's ids;
 // pair i = (t - t0) * k + j of the chunk gets its expert in pair_exp[i].
 MOE_DEV void route_chunk(const RouteParams& p, int64_t t0, int ntok, int npl, int* pair_exp,
-                         float (*sel_v)[kMaxTopk], int (*sel_i)[kMaxTopk]) {
+                         float (*sel_v)[kMaxTopk], int (*sel_i)[kMaxTopk],
+                         uint64_t (*sel_k)[kMaxTopk]) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int k = p.topk;
@@ -156,11 +183,11 @@ MOE_DEV void route_chunk(const RouteParams& p, int64_t t0, int ntok, int npl, in
             const float* lr = p.logits + t * p.E;
             int32_t* io = p.idx_out + t * k;
             float* wo = p.w_out + t * k;
-            if (npl <= 1) route_token<1>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], pair_exp + i * k);
-            else if (npl <= 2) route_token<2>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], pair_exp + i * k);
-            else if (npl <= 4) route_token<4>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], pair_exp + i * k);
-            else if (npl <= 8) route_token<8>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], pair_exp + i * k);
-            else route_token<16>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], pair_exp + i * k);
+            if (npl <= 1) route_token<1>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], sel_k[wave], pair_exp + i * k);
+            else if (npl <= 2) route_token<2>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], sel_k[wave], pair_exp + i * k);
+            else if (npl <= 4) route_token<4>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], sel_k[wave], pair_exp + i * k);
+            else if (npl <= 8) route_token<8>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], sel_k[wave], pair_exp + i * k);
+            else route_token<16>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], sel_k[wave], pair_exp + i * k);
         }
     } else {
         for (int i = tid; i < ntok * k; i += kRouteThreads) {
@@ -180,6 +207,7 @@ MOE_DEV void route_count_block(const RouteParams& p, int npl) {
     __shared__ int base[kMaxExperts];
     __shared__ float sel_v[kRouteWaves][kMaxTopk];
     __shared__ int sel_i[kRouteWaves][kMaxTopk];
+    __shared__ uint64_t sel_k[kRouteWaves][kMaxTopk];
     __shared__ int pair_rank[kRouteTokensPerBlock * kMaxTopk];
     __shared__ int pair_exp[kRouteTokensPerBlock * kMaxTopk];   // expert of pair i of this block
 
@@ -190,7 +218,7 @@ MOE_DEV void route_count_block(const RouteParams& p, int npl) {
 
     for (int e = tid; e < p.E; e += kRouteThreads) hist[e] = 0;
     // 1. routing (one wave per token) or caller's ids
-    route_chunk(p, t0, ntok, npl, pair_exp, sel_v, sel_i);
+    route_chunk(p, t0, ntok, npl, pair_exp, sel_v, sel_i, sel_k);
     __syncthreads();
 
     // 2. count: LDS histogram; the LDS atomic's return is the pair's rank here
@@ -215,36 +243,29 @@ MOE_DEV void route_count_block(const RouteParams& p, int npl) {
 // tokens each; every block then quantises its grid-stride share of x.
 __global__ __launch_bounds__(kRouteThreads) void route_count_quant_kernel(RouteParams p, int npl) {
     if ((int64_t)blockIdx.x * kRouteTokensPerBlock < p.T) route_count_block(p, npl);
-    if (p.x) quant_rows(p);
+    if (p.x) quant_rows(p, blockIdx.x, gridDim.x);
 }
 
-// Exclusive scan of n <= 1024 ints in LDS by a 256-thread block: out[0..n].
-MOE_DEV void block_exclusive_scan(const int* in, int* out, int n, int* tmp) {
+using BlockScan = rocprim::block_scan<int, kRouteThreads>;
+
+// Exclusive scan of n <= 1024 ints in LDS by a 256-thread block: out[0..n]
+// (out[n] = total).  Ends with a barrier, so st may be reused right away.
+MOE_DEV void block_exclusive_scan(const int* in, int* out, int n, BlockScan::storage_type& st) {
     const int tid = threadIdx.x;
-    int v[4];
-    int s = 0;
+    int v[4], o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        int i = tid * 4 + j;
+        const int i = tid * 4 + j;
         v[j] = i < n ? in[i] : 0;
-        s += v[j];
     }
-    tmp[tid] = s;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-        int a = tid >= o ? tmp[tid - o] : 0;
-        __syncthreads();
-        tmp[tid] += a;
-        __syncthreads();
-    }
-    int run = tmp[tid] - s;
+    int total;
+    BlockScan().exclusive_scan(v, o, 0, total, st);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        int i = tid * 4 + j;
-        if (i < n) out[i] = run;
-        run += v[j];
+        const int i = tid * 4 + j;
+        if (i < n) out[i] = o[j];
     }
-    if (tid == 255) out[n] = tmp[255];
+    if (tid == 0) out[n] = total;
     __syncthreads();
 }
 
@@ -254,7 +275,7 @@ MOE_DEV void block_exclusive_scan(const int* in, int* out, int n, int* tmp) {
 // expert ceil(count / rows) tiles, prefix-summed, one record per tile
 // {expert, first position, rows}, zero records up to the table's size.
 MOE_DEV void write_tables(const ScatterParams& p, const int* cnt, const int* off, int* tiles,
-                          int* toff, int* tmp) {
+                          int* toff, BlockScan::storage_type& tmp) {
     const int tid = threadIdx.x;
     for (int e = tid; e < p.E; e += kRouteThreads) p.counts_out[e] = cnt[e];
     for (int e = tid; e <= p.E; e += kRouteThreads) p.offsets_out[e] = off[e];
@@ -294,7 +315,7 @@ __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p)
     __shared__ int off[kMaxExperts + 1];
     __shared__ int tiles[kMaxExperts];
     __shared__ int toff[kMaxExperts + 1];
-    __shared__ int tmp[256];
+    __shared__ BlockScan::storage_type tmp;
     __shared__ int last;
     const int tid = threadIdx.x;
     for (int e = tid; e < p.E; e += kRouteThreads)
@@ -332,8 +353,8 @@ __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p)
 // pairs in an LDS histogram whose atomic returns each pair's rank inside its
 // expert, scans the counts, writes the tables and scatters the pairs, with no
 // global counters and no second launch ("05.10 Counting Sort /
-// Bucketization" 2.1-2.3 inside one workgroup).  Every workgroup quantises its
-// grid-stride share of x.
+// Bucketization" 2.1-2.3 inside one workgroup).  The other workgroups
+// quantise x meanwhile.
 __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(RouteParams rp, ScatterParams sp,
                                                                     int npl) {
     if (blockIdx.x == 0) {
@@ -341,16 +362,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(RouteParams 
         __shared__ int off[kMaxExperts + 1];
         __shared__ int tiles[kMaxExperts];
         __shared__ int toff[kMaxExperts + 1];
-        __shared__ int tmp[256];
+        __shared__ BlockScan::storage_type tmp;
         __shared__ float sel_v[kRouteWaves][kMaxTopk];
         __shared__ int sel_i[kRouteWaves][kMaxTopk];
+        __shared__ uint64_t sel_k[kRouteWaves][kMaxTopk];
         __shared__ int pair_exp[kSmallPairs];
         __shared__ int pair_rank[kSmallPairs];
         const int tid = threadIdx.x;
         const int k = rp.topk;
         const int npairs = (int)rp.T * k;
         for (int e = tid; e < rp.E; e += kRouteThreads) hist[e] = 0;
-        route_chunk(rp, 0, (int)rp.T, npl, pair_exp, sel_v, sel_i);
+        route_chunk(rp, 0, (int)rp.T, npl, pair_exp, sel_v, sel_i, sel_k);
         __syncthreads();
         for (int i = tid; i < npairs; i += kRouteThreads) {
             const int e = pair_exp[i];
@@ -369,14 +391,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(RouteParams 
             }
         }
         write_tables(sp, hist, off, tiles, toff, tmp);
+        if (gridDim.x > 1) return;                    // the other workgroups quantise x
     }
-    if (rp.x) quant_rows(rp);
+    if (rp.x) {
+        const int b = gridDim.x > 1 ? (int)blockIdx.x - 1 : 0;
+        quant_rows(rp, b, gridDim.x > 1 ? (int)gridDim.x - 1 : 1);
+    }
 }
 
 hipError_t launch_route(const RouteParams& rp, const ScatterParams& sp, hipStream_t s) {
     if (rp.T > 0 && rp.T * rp.topk <= kSmallPairs) {
-        int64_t quant_blocks = rp.x ? (rp.T * (rp.H / 8) + 4 * kRouteThreads - 1) / (4 * kRouteThreads) : 1;
-        dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(quant_blocks, 2048)));
+        // workgroup 0 routes and buckets; the others quantise x
+        int64_t quant_blocks = rp.x ? (rp.T * (rp.H / 8) + 2 * kRouteThreads - 1) / (2 * kRouteThreads) : 0;
+        dim3 grid((unsigned)(1 + std::min<int64_t>(quant_blocks, 2048)));
         const int npl = rp.logits ? (rp.E + 63) / 64 : 1;
         hipLaunchKernelGGL(route_small_kernel, grid, dim3(kRouteThreads), 0, s, rp, sp, npl);
         return hipGetLastError();

@@ -110,6 +110,26 @@ def test_route_bit_exact(name):
     assert np.array_equal(out2["counts"].cpu().numpy(), got["counts"])
 
 
+@pytest.mark.parametrize("T,E,topk", [(40, 64, 8), (600, 256, 8), (5, 1024, 16)])
+def test_route_ties_bit_exact(T, E, topk):
+    """Logits with many equal values (small integers, +0 and -0): the slots follow
+    decreasing logit, equal logits by increasing expert id."""
+    _log(f"route ties T={T} E={E} k={topk}")
+    m = G.lib()
+    d = m.dims(T, 128, 128, E, topk)
+    ws = m.new_workspace(d)
+    rng = np.random.default_rng(11)
+    logits = rng.integers(-2, 3, (T, E)).astype(np.float32)
+    logits[rng.random((T, E)) < 0.3] = -0.0
+    out = m.route(d, G.to_dev(logits), ws)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    idx, wt = M.route(logits, topk)
+    assert np.array_equal(got["topk_idx"], idx)
+    np.testing.assert_allclose(got["topk_w"], wt, rtol=4e-6, atol=1e-7)
+    G.check_bucketize(got, idx, E)
+
+
 # ------------------------------------------------------------------ whole layer
 
 @pytest.mark.parametrize("w", SMALL_SHAPES, ids=lambda w: w.name)
