@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-sample-experts", type=int, default=1,
                     help="experts whose rows the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gemm-path", choices=("auto", "narrow", "tiled", "one-launch"),
+                    default="auto", help="GEMM kernels moe_forward uses (default: its own choice)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before the timed steps, copy a buffer of this many MiB once (a "
                          "plain copy kernel of known size, to calibrate traffic counters)")
@@ -144,14 +146,21 @@ def gemm1_algorithmic_bytes(w, counts) -> float:
     return touched * w13 + w.T * (w.H + w.H // 32) + R * (w.I + w.I // 32)
 
 
-def gemm1_kernel_name(w) -> str:
-    if w.T * w.topk <= NARROW_ROWS_PER_EXPERT * w.E:
+def gemm1_kernel_name(w, path) -> str:
+    if path == "narrow" or (path == "auto" and w.T * w.topk <= NARROW_ROWS_PER_EXPERT * w.E):
         return "narrow_gemm_kernel<GEMM1> (weight-streaming FP8xFP4 MFMA + SwiGLU*w -> FP8)"
     return "grouped_gemm_kernel<GEMM1> (tiled FP8xFP4 MFMA + SwiGLU*w -> FP8)"
 
 
-def roofline(w, counts, gemm1_ms):
-    kernel = gemm1_kernel_name(w)
+def roofline(w, counts, gemm1_ms, path="auto"):
+    if path == "one-launch":
+        # GEMM1 and GEMM2 in one kernel: all the layer's GEMM FLOPs over its duration
+        tflops = w.flops() / (gemm1_ms * 1e-3) / 1e12
+        return {"kernel": "fused_gemm_kernel (GEMM1 + SwiGLU*w + GEMM2, one launch)",
+                "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_FP8_TFLOPS, 4),
+                "traffic": None, "alg_bytes": None}
+    kernel = gemm1_kernel_name(w, path)
     traffic = read_traffic(w.name)
     alg_bytes = gemm1_algorithmic_bytes(w, counts)
     if w.name in HBM_BOUND:
@@ -238,9 +247,11 @@ def main():
     hip = Hip()
     nstage = m.NUM_STAGE_EVENTS
     ev = [(ctypes.c_void_p * nstage)(*[hip.event() for _ in range(nstage)]) for _ in range(a.steps)]
-    args_plain = m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits)
-    args_ev = [m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, stage_events=e)
-               for e in ev]
+    flags = {"auto": m.FLAG_NONE, "narrow": m.FLAG_NARROW, "tiled": m.FLAG_TILED,
+             "one-launch": m.FLAG_ONE_LAUNCH}[a.gemm_path]
+    args_plain = m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, flags=flags)
+    args_ev = [m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, flags=flags,
+                              stage_events=e) for e in ev]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     if a.calib_copy_mb:
@@ -293,7 +304,7 @@ def main():
         "layer_tflops": round(layer_tflops, 2),
         "layer_frac_mfma": round(layer_tflops / PEAK_MFMA_FP8_TFLOPS, 4),
         "stages_ms": {n: round(float(v), 4) for n, v in zip(m.STAGES, stage_ms)},
-        "roofline": roofline(w, counts, float(stage_ms[1])),
+        "roofline": roofline(w, counts, float(stage_ms[1]), a.gemm_path),
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_experts)

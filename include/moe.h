@@ -76,11 +76,18 @@ typedef struct moe_dims {
  * output tiles staged through LDS, for many rows per expert) or as narrow
  * kernels (weights streamed from HBM straight into registers over many small
  * workgroups, for few rows per expert, the decode regime).  By default
- * moe_forward takes the narrow kernels when T * topk <= 16 * E.  Both give
- * identical results; the flags force one (setting both is MOE_EINVAL). */
+ * moe_forward takes the narrow kernels when T * topk <= 16 * E, else the tiled
+ * GEMM1 and GEMM2 as two launches ordered by the stream.  MOE_FLAG_ONE_LAUNCH
+ * runs the tiled GEMM1 -> SwiGLU -> GEMM2 as one persistent launch whose GEMM2
+ * tiles wait on per-m-tile ready counters, experts grouped in waves ("MegaMoE"
+ * notes, "Scheduler" and "Wave"); on one MI355X it measured slower than the
+ * two launches at the DeepSeek-V3-like and 256-expert shapes, so it is not
+ * the default.  All paths meet the same tolerance against the definition.
+ * NARROW together with TILED or ONE_LAUNCH is MOE_EINVAL. */
 #define MOE_FLAG_NONE 0u
 #define MOE_FLAG_NARROW 1u
 #define MOE_FLAG_TILED 2u
+#define MOE_FLAG_ONE_LAUNCH 4u
 
 #define MOE_NUM_STAGE_EVENTS 5
 
@@ -101,7 +108,9 @@ typedef struct moe_dims {
  *             workspace must not be used by two calls that may overlap.
  *   stage_events  NULL, or MOE_NUM_STAGE_EVENTS caller-created HIP events that
  *             are recorded on s before routing, before GEMM1, before GEMM2,
- *             before the combine and after it (for per-stage timing). */
+ *             before the combine and after it (for per-stage timing); with
+ *             MOE_FLAG_ONE_LAUNCH the third is recorded after that launch,
+ *             right before the fourth. */
 typedef struct moe_args {
     moe_dims_t dims;
     const uint16_t* x;
@@ -131,10 +140,14 @@ typedef struct moe_args {
  *   slot_of   int32 [T, topk]     position of pair (t, j), -1 when skipped
  *   xq, xsf   uint8 [T, H], [H/128, T, 4]        quantised x (scales K-step major)
  *   hq, hsf   uint8 [T*topk, I], [I/128, T*topk, 4]  quantised h by position
- *   o         BF16 [T*topk, H]                  GEMM2 rows by position */
+ *   o         BF16 [T*topk, H]                  GEMM2 rows by position
+ *   status    int32 [1]   nonzero if a wait of the one-launch GEMMs gave up in
+ *                         the last call (its output is then invalid); every
+ *                         call clears it before its GEMMs */
 typedef struct moe_layout {
     size_t topk_idx, topk_w, counts, offsets, slot_src, slot_of;
     size_t xq, xsf, hq, hsf, o;
+    size_t status;
     size_t total;
 } moe_layout_t;
 

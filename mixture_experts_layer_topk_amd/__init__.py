@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
-FLAG_NONE, FLAG_NARROW, FLAG_TILED = 0, 1, 2
+FLAG_NONE, FLAG_NARROW, FLAG_TILED, FLAG_ONE_LAUNCH = 0, 1, 2, 4
 
 
 class MoeError(RuntimeError):
@@ -48,7 +48,7 @@ STAGES = ("route+quant", "gemm1", "gemm2", "combine")
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("topk_idx", "topk_w", "counts", "offsets", "slot_src", "slot_of",
-                 "xq", "xsf", "hq", "hsf", "o", "total")]
+                 "xq", "xsf", "hq", "hsf", "o", "status", "total")]
 
 
 # Every symbol include/moe.h declares.
@@ -195,7 +195,8 @@ def forward_raw(args: Args, stream=None):
 def forward(d: Dims, x, w13, w13_sf, w2, w2_sf, ws, logits=None, topk_idx=None, topk_w=None,
             y=None, flags=FLAG_NONE):
     """The whole layer; returns y (BF16 [T, H]).  flags: FLAG_NARROW / FLAG_TILED force
-    the GEMM kernel family (default: chosen from the rows per expert)."""
+    the GEMM kernel family (default: chosen from the rows per expert); FLAG_ONE_LAUNCH
+    runs the tiled GEMMs as one launch with ready counters."""
     if y is None:
         y = torch.empty((d.T, d.H), dtype=torch.bfloat16, device=x.device)
     forward_raw(forward_args(d, x, w13, w13_sf, w2, w2_sf, y, ws, logits, topk_idx, topk_w,
@@ -226,4 +227,5 @@ def intermediates(d: Dims, ws: torch.Tensor):
         hq=view(L.hq, R * I, torch.uint8, (R, I)),
         hsf=view(L.hsf, R * I // 32, torch.uint8, (I // 128, R, 4)).permute(1, 0, 2).reshape(R, I // 32),
         o=view(L.o, R * H, torch.int16, (R, H)),
+        status=view(L.status, 1, torch.int32, (1,)),
     )

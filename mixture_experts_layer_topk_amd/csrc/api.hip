@@ -21,8 +21,8 @@ constexpr int64_t kNarrowRowsPerExpert = 16;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Carve {
-    size_t cnt, arrive, counts, offsets, mtile_off, mtile_e, mtile_rec, sub_rec, nsub, topk_idx,
-        topk_w, slot_in_e, slot_src, slot_of;
+    size_t cnt, arrive, status, counts, offsets, mtile_off, mtile_e, mtile_rec, sub_rec, nsub, ready,
+        topk_idx, topk_w, slot_in_e, slot_src, slot_of;
     size_t xq, xsf, hq, hsf, o, total;
 };
 
@@ -44,8 +44,11 @@ Carve carve(const moe_dims_t& d) {
     const size_t T = (size_t)d.T, E = (size_t)d.E, k = (size_t)d.topk, R = T * k;
     size_t at = 0;
     auto take = [&](size_t bytes) { size_t off = at; at = align_up(at + bytes); return off; };
-    c.cnt = take(E * 4);
+    // counters first, at offsets that do not depend on the shape: a workspace can
+    // serve calls of different shapes after one moe_workspace_init
+    c.cnt = take(moe::kMaxExpertsCap * 4);
     c.arrive = take(64);
+    c.status = take(64);
     c.counts = take(E * 4);
     c.offsets = take((E + 1) * 4);
     c.mtile_off = take((E + 1) * 4);
@@ -53,6 +56,7 @@ Carve carve(const moe_dims_t& d) {
     c.mtile_rec = take((max_mtiles(d) + 1) * 16);
     c.sub_rec = take((max_subs(d) + 1) * 16);
     c.nsub = take(4);
+    c.ready = take(max_mtiles(d) * 4);
     c.topk_idx = take(R * 4);
     c.topk_w = take(R * 4);
     c.slot_in_e = take(R * 4);
@@ -121,6 +125,7 @@ int moe_workspace_layout(const moe_dims_t* d, moe_layout_t* out) {
     out->hq = c.hq;
     out->hsf = c.hsf;
     out->o = c.o;
+    out->status = c.status;
     out->total = c.total;
     return MOE_OK;
 }
@@ -176,6 +181,8 @@ int moe_route(const moe_dims_t* d, const float* logits, int32_t* topk_idx, float
     sp.sub_rec = at<int4>(ws, c.sub_rec);
     sp.nsub = at<int32_t>(ws, c.nsub);
     sp.max_subs = (int)max_subs(*d);
+    sp.ready = at<int>(ws, c.ready);
+    sp.status = at<int>(ws, c.status);
     hipError_t err = moe::launch_route(rp, sp, s);
     return err == hipSuccess ? MOE_OK : hip_fail(err);
 }
@@ -215,8 +222,10 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     if (d.T == 0) return MOE_OK;
     if (!a->x || !a->w13 || !a->w13_sf || !a->w2 || !a->w2_sf || !a->y || !a->ws) return MOE_EINVAL;
     if (!a->logits && (!a->topk_idx || !a->topk_w)) return MOE_EINVAL;
-    if ((a->flags & ~(MOE_FLAG_NARROW | MOE_FLAG_TILED)) ||
-        (a->flags & (MOE_FLAG_NARROW | MOE_FLAG_TILED)) == (MOE_FLAG_NARROW | MOE_FLAG_TILED))
+    if ((a->flags & ~(MOE_FLAG_NARROW | MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH)) ||
+        (a->flags & (MOE_FLAG_NARROW | MOE_FLAG_TILED)) == (MOE_FLAG_NARROW | MOE_FLAG_TILED) ||
+        (a->flags & (MOE_FLAG_NARROW | MOE_FLAG_ONE_LAUNCH)) ==
+            (MOE_FLAG_NARROW | MOE_FLAG_ONE_LAUNCH))
         return MOE_EINVAL;
     if (!aligned16(a->x) || !aligned16(a->w13) || !aligned16(a->w2) || !aligned16(a->y) ||
         ((uintptr_t)a->w13_sf & 3) || ((uintptr_t)a->w2_sf & 3))
@@ -262,6 +271,8 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     sp.sub_rec = at<int4>(ws, c.sub_rec);
     sp.nsub = at<int32_t>(ws, c.nsub);
     sp.max_subs = (int)max_subs(d);
+    sp.ready = at<int>(ws, c.ready);
+    sp.status = at<int>(ws, c.status);
     hipEvent_t* ev = a->stage_events;
     hipError_t err = ev ? hipEventRecord(ev[0], s) : hipSuccess;
     if (err == hipSuccess) err = moe::launch_route(rp, sp, s);
@@ -274,6 +285,8 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     gp.mtile_rec = sp.mtile_rec;
     gp.sub_rec = sp.sub_rec;
     gp.nsub = sp.nsub;
+    gp.ready = at<int>(ws, c.ready);
+    gp.status = at<int>(ws, c.status);
     gp.slot_src = sp.slot_src;
     gp.topk_w = rp.w_out;
     gp.xq = rp.xq;
@@ -296,11 +309,18 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     // few rows per expert on average: the weight-streaming (narrow) kernels
     bool narrow = R <= kNarrowRowsPerExpert * (int64_t)d.E;
     if (a->flags & MOE_FLAG_NARROW) narrow = true;
-    if (a->flags & MOE_FLAG_TILED) narrow = false;
+    if (a->flags & (MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH)) narrow = false;
+    const bool fused = (a->flags & MOE_FLAG_ONE_LAUNCH) != 0;
     if (ev) err = hipEventRecord(ev[1], s);
-    if (err == hipSuccess) err = narrow ? moe::launch_narrow_gemm1(gp, s) : moe::launch_gemm1(gp, s);
-    if (err == hipSuccess && ev) err = hipEventRecord(ev[2], s);
-    if (err == hipSuccess) err = narrow ? moe::launch_narrow_gemm2(gp, s) : moe::launch_gemm2(gp, s);
+    if (fused) {
+        // GEMM1 -> SwiGLU -> GEMM2 in one launch: both events after it
+        if (err == hipSuccess) err = moe::launch_fused_gemm(gp, s);
+        if (err == hipSuccess && ev) err = hipEventRecord(ev[2], s);
+    } else {
+        if (err == hipSuccess) err = narrow ? moe::launch_narrow_gemm1(gp, s) : moe::launch_gemm1(gp, s);
+        if (err == hipSuccess && ev) err = hipEventRecord(ev[2], s);
+        if (err == hipSuccess) err = narrow ? moe::launch_narrow_gemm2(gp, s) : moe::launch_gemm2(gp, s);
+    }
     if (err == hipSuccess && ev) err = hipEventRecord(ev[3], s);
     if (err == hipSuccess) err = moe::launch_combine(gp.o, sp.slot_of, d.T, d.topk, d.H, a->y, s);
     if (err == hipSuccess && ev) err = hipEventRecord(ev[4], s);

@@ -132,28 +132,33 @@ MOE_DEV void barrier_nofence() {
 // the 16 lanes of one lane group read 256 consecutive bytes (no conflicts).
 MOE_DEV int scale_slot_row(int q) { return (q & ~63) | ((q & 3) << 4) | ((q >> 2) & 15); }
 
+// kAux: cache policy bits of the load (kCohAux: device-coherent, sc1)
+constexpr int kCohAux = 16;
+constexpr int kSpinLimit = 1 << 24;     // polls of a ready counter before giving up (~0.5 s)
+
+template <int kAux>
 MOE_DEV void load_lds16(const void* g, uint8_t* lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, kAux);
 }
+template <int kAux>
 MOE_DEV void load_lds4(const void* g, uint8_t* lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 4, 0, kAux);
 }
 
-template <int BM, int BN, int WM, int WN, bool kG1>
-__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParams p) {
+// One BM x BN output tile of GEMM1 (kG1) or GEMM2 over all of K, epilogue
+// included.  kCoh: the tile runs inside the one-launch kernel, where GEMM2 reads
+// h that other XCDs wrote in the same launch; h is then stored and read with
+// device-coherent accesses (sc1), which go to the memory-side cache instead of
+// an XCD's own L2, while the weights keep the cached path.
+template <int BM, int BN, int WM, int WN, bool kG1, bool kCoh>
+MOE_DEV void gemm_tile(const GemmParams& p, int mt_g, int ntile, uint8_t* smem, int* s_tile) {
     using C = Cfg<BM, BN, WM, WN, kG1>;
-    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    constexpr int kAuxA = (kCoh && !kG1) ? kCohAux : 0;
     int* s_tok = reinterpret_cast<int*>(smem + C::kStages * C::kStage);   // [BM] A row source
     float* s_w = reinterpret_cast<float*>(s_tok + BM);                     // [BM] topk weight
-    __shared__ int s_tile[4];
-
     const int tid = threadIdx.x;
-
     const int K = kG1 ? p.H : p.I;                 // reduction length
     const int nk = K / BK;
-    // n-tiles: GEMM1 covers BN/2 columns of I (gate and up), GEMM2 BN columns of H;
-    // the last one may be partial (I and H are multiples of 128)
-    const int NTILES = kG1 ? (p.I + BN / 2 - 1) / (BN / 2) : (p.H + BN - 1) / BN;
     // Scales are stored K-step major: the 4 UE8M0 bytes of one 128-wide K step
     // for row r sit at slab[ks][r][0..3], so a tile's scales for one K step are
     // 4-byte entries of one slab rather than bytes strided across the rows.
@@ -162,283 +167,386 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
     const uint8_t* a_base = kG1 ? p.xq : p.hq;
     const uint8_t* sa_base = kG1 ? p.xsf : p.hsf;
 
-    if (tid == 0) s_tile[3] = p.mtile_off[p.E];
+    // Per-lane indices are re-derived from an opaque copy of the thread id in
+    // every tile, so the compiler recomputes the (cheap) per-lane constants
+    // here instead of keeping dozens of them alive across the K loop.
+    int tid_v = tid;
+    asm volatile("" : "+v"(tid_v));
+    const int lane = tid_v & 63;
+    const int wave = tid_v >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int l16 = lane & 15, lg = lane >> 4;
+    if (tid == 0) {
+        const int4 rec = p.mtile_rec[mt_g];      // {expert, first position, rows}
+        s_tile[0] = rec.x;
+        s_tile[1] = rec.y;
+        s_tile[2] = rec.z;
+    }
     __syncthreads();
-    const int mtiles = s_tile[3];
-    const int total = mtiles * NTILES;
-    const int grid = gridDim.x;
-    const int slot = (grid % kXCDs) == 0
-                         ? (blockIdx.x % kXCDs) * (grid / kXCDs) + blockIdx.x / kXCDs
-                         : blockIdx.x;
+    const int e = s_tile[0];
+    const int p0 = s_tile[1];
+    const int valid = s_tile[2];
 
-    for (int tile = slot; tile < total; tile += grid) {
-        // Per-lane indices are re-derived from an opaque copy of the thread id in
-        // every tile, so the compiler recomputes the (cheap) per-lane constants
-        // here instead of keeping dozens of them alive across the K loop.
-        int tid_v = tid;
-        asm volatile("" : "+v"(tid_v));
-        const int lane = tid_v & 63;
-        const int wave = tid_v >> 6;
-        const int wm = wave / WN, wn = wave % WN;
-        const int l16 = lane & 15, lg = lane >> 4;
-        const int grp = tile / (kGM * NTILES);
-        const int gm = min(kGM, mtiles - grp * kGM);      // m-tiles in this group
-        const int in_grp = tile - grp * (kGM * NTILES);
-        const int ntile = in_grp / gm;
-        const int mt_g = grp * kGM + (in_grp - ntile * gm);
-        if (tid == 0) {
-            const int e = p.mtile_e[mt_g];
-            s_tile[0] = e;
-            s_tile[1] = p.offsets[e] + (mt_g - p.mtile_off[e]) * BM;
-            s_tile[2] = p.offsets[e + 1];
+    // row sources of the A tile: token rows (GEMM1) or positions (GEMM2)
+    if (tid < BM) {
+        int pr = p0 + min(tid, valid - 1);
+        if (kG1) {
+            int src = p.slot_src[pr];
+            s_tok[tid] = src / p.topk;
+            s_w[tid] = p.topk_w[src];
+        } else {
+            s_tok[tid] = pr;
         }
-        __syncthreads();
-        const int e = s_tile[0];
-        const int p0 = s_tile[1];
-        const int valid = min(BM, s_tile[2] - p0);
+    }
+    __syncthreads();
 
-        // row sources of the A tile: token rows (GEMM1) or positions (GEMM2)
-        if (tid < BM) {
-            int pr = p0 + min(tid, valid - 1);
-            if (kG1) {
-                int src = p.slot_src[pr];
-                s_tok[tid] = src / p.topk;
-                s_w[tid] = p.topk_w[src];
-            } else {
-                s_tok[tid] = pr;
-            }
+    // B tile LDS row -> weight row.  Inside a wave's slice, LDS row nt*16 + c
+    // holds output column c*NT + nt (GEMM2) or, for GEMM1, I column
+    // c*NT/2 + nt/2 of the gate (even nt) or up (odd nt) projection.
+    auto b_row = [&](int b) -> int {
+        int ws = b / C::WTN, bl = b % C::WTN;
+        int nt = bl >> 4, c = bl & 15;
+        if (kG1) {
+            int icol = ntile * (BN / 2) + ws * (C::WTN / 2) + c * (C::NT / 2) + (nt >> 1);
+            icol = min(icol, p.I - 1);          // partial last n-tile: never stored
+            return (nt & 1) ? p.I + icol : icol;
+        } else {
+            int n = ntile * BN + ws * C::WTN + c * C::NT + nt;
+            return min(n, p.H - 1);
         }
-        __syncthreads();
+    };
+    const int64_t b_stride = K / 2;
+    const uint8_t* w_base = kG1 ? p.w13 + (int64_t)e * (2 * p.I) * b_stride
+                                : p.w2 + (int64_t)e * p.H * b_stride;
+    const uint8_t* wsf_base = (kG1 ? p.w13sf : p.w2sf) + (int64_t)e * nk * sb_slab;
 
-        // B tile LDS row -> weight row.  Inside a wave's slice, LDS row nt*16 + c
-        // holds output column c*NT + nt (GEMM2) or, for GEMM1, I column
-        // c*NT/2 + nt/2 of the gate (even nt) or up (odd nt) projection.
-        auto b_row = [&](int b) -> int {
-            int ws = b / C::WTN, bl = b % C::WTN;
-            int nt = bl >> 4, c = bl & 15;
-            if (kG1) {
-                int icol = ntile * (BN / 2) + ws * (C::WTN / 2) + c * (C::NT / 2) + (nt >> 1);
-                icol = min(icol, p.I - 1);          // partial last n-tile: never stored
-                return (nt & 1) ? p.I + icol : icol;
-            } else {
-                int n = ntile * BN + ws * C::WTN + c * C::NT + nt;
-                return min(n, p.H - 1);
-            }
-        };
-        const int64_t b_stride = K / 2;
-        const uint8_t* w_base = kG1 ? p.w13 + (int64_t)e * (2 * p.I) * b_stride
-                                    : p.w2 + (int64_t)e * p.H * b_stride;
-        const uint8_t* wsf_base = (kG1 ? p.w13sf : p.w2sf) + (int64_t)e * nk * sb_slab;
-
-        // per-lane global sources of each load instruction (fixed over K), as
-        // 32-bit byte offsets from wave-uniform bases
-        uint32_t a_src[C::kAI];
+    // per-lane global sources of each load instruction (fixed over K), as
+    // 32-bit byte offsets from wave-uniform bases
+    uint32_t a_src[C::kAI];
 #pragma unroll
-        for (int j = 0; j < C::kAI; ++j) {
-            int r = 8 * (j * C::kWaves + wave) + (lane >> 3);
-            int c = (lane & 7) ^ a_swz(r);
-            a_src[j] = (uint32_t)s_tok[r] * (uint32_t)K + c * 16;
+    for (int j = 0; j < C::kAI; ++j) {
+        int r = 8 * (j * C::kWaves + wave) + (lane >> 3);
+        int c = (lane & 7) ^ a_swz(r);
+        a_src[j] = (uint32_t)s_tok[r] * (uint32_t)K + c * 16;
+    }
+    uint32_t b_src[C::kBI];
+#pragma unroll
+    for (int j = 0; j < C::kBI; ++j) {
+        int n = 16 * (j * C::kWaves + wave) + (lane >> 2);
+        int c = (lane & 3) ^ b_swz(n);
+        b_src[j] = (uint32_t)b_row(n) * (uint32_t)b_stride + c * 16;
+    }
+    // 64-row block of scale load j of this wave (wrapping when the tile is short)
+    auto sa_blk = [&](int j) { return (j * C::kWaves + wave) % (C::kSARows / 64); };
+    auto sb_blk = [&](int j) { return (j * C::kWaves + wave) % (C::kSBRows / 64); };
+    uint32_t sa_src[C::kSAI];
+#pragma unroll
+    for (int j = 0; j < C::kSAI; ++j)
+        sa_src[j] = (uint32_t)s_tok[scale_slot_row(64 * sa_blk(j) + lane)] * 4u;
+    // B scales are staged in the B tile's LDS row order, regrouped by
+    // scale_slot_row: the slots of LDS row q hold weight row b_row(q).
+    uint32_t sb_src[C::kSBI];
+#pragma unroll
+    for (int j = 0; j < C::kSBI; ++j)
+        sb_src[j] = (uint32_t)b_row(scale_slot_row(64 * sb_blk(j) + lane)) * 4u;
+
+    // Load instruction j (of kLoads) of K slice ks into LDS stage `stage`:
+    // A tile chunks first, then B, then the two scale tiles.
+    auto issue_one = [&](int j, int ks, int stage) {
+        uint8_t* sA = smem + stage * C::kStage;
+        uint8_t* sB = sA + C::kABytes;
+        uint8_t* sSA = sB + C::kBBytes;
+        uint8_t* sSB = sSA + C::kSABytes;
+        if (j < C::kAI) {
+            load_lds16<kAuxA>(a_base + ks * BK + a_src[j], sA + (j * C::kWaves + wave) * 1024);
+        } else if (j < C::kAI + C::kBI) {
+            const int jb = j - C::kAI;
+            load_lds16<0>(w_base + ks * (BK / 2) + b_src[jb], sB + (jb * C::kWaves + wave) * 1024);
+        } else if (j < C::kAI + C::kBI + C::kSAI) {
+            const int js = j - C::kAI - C::kBI;
+            load_lds4<kAuxA>(sa_base + ks * sa_slab + sa_src[js], sSA + sa_blk(js) * 256);
+        } else {
+            const int js = j - C::kAI - C::kBI - C::kSAI;
+            load_lds4<0>(wsf_base + ks * sb_slab + sb_src[js], sSB + sb_blk(js) * 256);
         }
-        uint32_t b_src[C::kBI];
+    };
+    auto issue = [&](int ks, int stage) {   // K slice ks into LDS stage
 #pragma unroll
-        for (int j = 0; j < C::kBI; ++j) {
-            int n = 16 * (j * C::kWaves + wave) + (lane >> 2);
-            int c = (lane & 3) ^ b_swz(n);
-            b_src[j] = (uint32_t)b_row(n) * (uint32_t)b_stride + c * 16;
+        for (int j = 0; j < C::kLoads; ++j) issue_one(j, ks, stage);
+    };
+
+    v4f acc[C::MT][C::NT];
+#pragma unroll
+    for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NT; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // MFMA operands.  Fragment addresses of different tiles differ by
+    // constants (the swizzles depend on row % 16 only).
+    const int a_row0 = wm * C::WTM + l16;
+    const int b_row0 = wn * C::WTN + l16;
+    const int a_lo = a_off(a_row0, lg), a_hi = a_off(a_row0, 4 + lg);
+    const int b_fr = C::kABytes + b_off(b_row0, lg);
+    // scale runs of this lane: tiles 4h .. 4h+3 at slot base + 64 h + 4 l16
+    const int sa_fr = C::kABytes + C::kBBytes + 4 * (wm * C::WTM + 4 * l16);
+    const int sb_fr = C::kABytes + C::kBBytes + C::kSABytes + 4 * (wn * C::WTN + 4 * l16);
+    static_assert(C::MT % 4 == 0 && C::NT % 4 == 0, "scale runs of four tiles");
+    v8i a[C::MT];
+    int sa[C::MT];
+    v4i b[C::NT];
+    int sb[C::NT];
+    auto read_a = [&](const uint8_t* st, int mt) {
+        v4i lo = *reinterpret_cast<const v4i*>(st + a_lo + mt * 16 * BK);
+        v4i hi = *reinterpret_cast<const v4i*>(st + a_hi + mt * 16 * BK);
+        a[mt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto read_b = [&](const uint8_t* st, int nt) {
+        b[nt] = *reinterpret_cast<const v4i*>(st + b_fr + nt * 16 * (BK / 2));
+    };
+    // lane group lg supplies the scale of K group lg: byte lg of each dword
+    auto read_scales = [&](const uint8_t* st) {
+#pragma unroll
+        for (int h = 0; h < C::MT / 4; ++h) {
+            const v4i v = *reinterpret_cast<const v4i*>(st + sa_fr + 256 * h);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sa[4 * h + t] = (int)((uint32_t)v[t] >> (8 * lg));
         }
-        // 64-row block of scale load j of this wave (wrapping when the tile is short)
-        auto sa_blk = [&](int j) { return (j * C::kWaves + wave) % (C::kSARows / 64); };
-        auto sb_blk = [&](int j) { return (j * C::kWaves + wave) % (C::kSBRows / 64); };
-        uint32_t sa_src[C::kSAI];
 #pragma unroll
-        for (int j = 0; j < C::kSAI; ++j)
-            sa_src[j] = (uint32_t)s_tok[scale_slot_row(64 * sa_blk(j) + lane)] * 4u;
-        // B scales are staged in the B tile's LDS row order, regrouped by
-        // scale_slot_row: the slots of LDS row q hold weight row b_row(q).
-        uint32_t sb_src[C::kSBI];
+        for (int h = 0; h < C::NT / 4; ++h) {
+            const v4i v = *reinterpret_cast<const v4i*>(st + sb_fr + 256 * h);
 #pragma unroll
-        for (int j = 0; j < C::kSBI; ++j)
-            sb_src[j] = (uint32_t)b_row(scale_slot_row(64 * sb_blk(j) + lane)) * 4u;
+            for (int t = 0; t < 4; ++t) sb[4 * h + t] = (int)((uint32_t)v[t] >> (8 * lg));
+        }
+    };
+    auto mma = [&](int mt, int nt) {
+        acc[mt][nt] = mfma_fp8_fp4(a[mt], b[nt], acc[mt][nt], sa[mt], sb[nt]);
+    };
 
-        // Load instruction j (of kLoads) of K slice ks into LDS stage `stage`:
-        // A tile chunks first, then B, then the two scale tiles.
-        auto issue_one = [&](int j, int ks, int stage) {
-            uint8_t* sA = smem + stage * C::kStage;
-            uint8_t* sB = sA + C::kABytes;
-            uint8_t* sSA = sB + C::kBBytes;
-            uint8_t* sSB = sSA + C::kSABytes;
-            if (j < C::kAI) {
-                load_lds16(a_base + ks * BK + a_src[j], sA + (j * C::kWaves + wave) * 1024);
-            } else if (j < C::kAI + C::kBI) {
-                const int jb = j - C::kAI;
-                load_lds16(w_base + ks * (BK / 2) + b_src[jb], sB + (jb * C::kWaves + wave) * 1024);
-            } else if (j < C::kAI + C::kBI + C::kSAI) {
-                const int js = j - C::kAI - C::kBI;
-                load_lds4(sa_base + ks * sa_slab + sa_src[js], sSA + sa_blk(js) * 256);
-            } else {
-                const int js = j - C::kAI - C::kBI - C::kSAI;
-                load_lds4(wsf_base + ks * sb_slab + sb_src[js], sSB + sb_blk(js) * 256);
-            }
-        };
-        auto issue = [&](int ks, int stage) {   // K slice ks into LDS stage
+    // Two waves per SIMD (8 waves): the SIMD's other wave runs its MFMAs
+    // while this one waits on LDS, the barrier or the load queue, so one
+    // K step is simply: read step ks's A fragments, then per n-tile its B
+    // fragment, its four MFMAs and one load of step ks + 2 into the stage
+    // every wave has retired (spreading the load issue between the MFMAs
+    // measured 5% faster than issuing them all first), then wait for this
+    // wave's loads of step ks + 1 and barrier.
+    auto step8 = [&](int ks) {
+        const uint8_t* cur = smem + (ks % C::kStages) * C::kStage;
+        const int ks2 = min(ks + 2, nk - 1), st2 = (ks + 2) % C::kStages;
+        read_scales(cur);
 #pragma unroll
-            for (int j = 0; j < C::kLoads; ++j) issue_one(j, ks, stage);
-        };
-
-        v4f acc[C::MT][C::NT];
+        for (int mt = 0; mt < C::MT; ++mt) read_a(cur, mt);
 #pragma unroll
-        for (int i = 0; i < C::MT; ++i)
+        for (int nt = 0; nt < C::NT; ++nt) {
+            read_b(cur, nt);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < C::NT; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-        // MFMA operands.  Fragment addresses of different tiles differ by
-        // constants (the swizzles depend on row % 16 only).
-        const int a_row0 = wm * C::WTM + l16;
-        const int b_row0 = wn * C::WTN + l16;
-        const int a_lo = a_off(a_row0, lg), a_hi = a_off(a_row0, 4 + lg);
-        const int b_fr = C::kABytes + b_off(b_row0, lg);
-        // scale runs of this lane: tiles 4h .. 4h+3 at slot base + 64 h + 4 l16
-        const int sa_fr = C::kABytes + C::kBBytes + 4 * (wm * C::WTM + 4 * l16);
-        const int sb_fr = C::kABytes + C::kBBytes + C::kSABytes + 4 * (wn * C::WTN + 4 * l16);
-        static_assert(C::MT % 4 == 0 && C::NT % 4 == 0, "scale runs of four tiles");
-        v8i a[C::MT];
-        int sa[C::MT];
-        v4i b[C::NT];
-        int sb[C::NT];
-        auto read_a = [&](const uint8_t* st, int mt) {
-            v4i lo = *reinterpret_cast<const v4i*>(st + a_lo + mt * 16 * BK);
-            v4i hi = *reinterpret_cast<const v4i*>(st + a_hi + mt * 16 * BK);
-            a[mt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        };
-        auto read_b = [&](const uint8_t* st, int nt) {
-            b[nt] = *reinterpret_cast<const v4i*>(st + b_fr + nt * 16 * (BK / 2));
-        };
-        // lane group lg supplies the scale of K group lg: byte lg of each dword
-        auto read_scales = [&](const uint8_t* st) {
-#pragma unroll
-            for (int h = 0; h < C::MT / 4; ++h) {
-                const v4i v = *reinterpret_cast<const v4i*>(st + sa_fr + 256 * h);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) sa[4 * h + t] = (int)((uint32_t)v[t] >> (8 * lg));
-            }
-#pragma unroll
-            for (int h = 0; h < C::NT / 4; ++h) {
-                const v4i v = *reinterpret_cast<const v4i*>(st + sb_fr + 256 * h);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) sb[4 * h + t] = (int)((uint32_t)v[t] >> (8 * lg));
-            }
-        };
-        auto mma = [&](int mt, int nt) {
-            acc[mt][nt] = mfma_fp8_fp4(a[mt], b[nt], acc[mt][nt], sa[mt], sb[nt]);
-        };
-
-        // Two waves per SIMD (8 waves): the SIMD's other wave runs its MFMAs
-        // while this one waits on LDS, the barrier or the load queue, so one
-        // K step is simply: read step ks's A fragments, then per n-tile its B
-        // fragment, its four MFMAs and one load of step ks + 2 into the stage
-        // every wave has retired (spreading the load issue between the MFMAs
-        // measured 5% faster than issuing them all first), then wait for this
-        // wave's loads of step ks + 1 and barrier.
-        auto step8 = [&](int ks) {
-            const uint8_t* cur = smem + (ks % C::kStages) * C::kStage;
-            const int ks2 = min(ks + 2, nk - 1), st2 = (ks + 2) % C::kStages;
-            read_scales(cur);
-#pragma unroll
-            for (int mt = 0; mt < C::MT; ++mt) read_a(cur, mt);
-#pragma unroll
-            for (int nt = 0; nt < C::NT; ++nt) {
-                read_b(cur, nt);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int mt = 0; mt < C::MT; ++mt) mma(mt, nt);
-                if (nt < C::kLoads) issue_one(nt, ks2, st2);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            static_assert(C::kLoads <= C::NT, "one load per n-tile group");
-            wait_vmcnt<C::kLoads>();
-            barrier_nofence();
-        };
-        static_assert(C::kWaves == 8, "the K-step schedule assumes two waves per SIMD");
-        wait_vmcnt<0>();
-        issue(0, 0);
-        issue(min(1, nk - 1), 1);
+            for (int mt = 0; mt < C::MT; ++mt) mma(mt, nt);
+            if (nt < C::kLoads) issue_one(nt, ks2, st2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        static_assert(C::kLoads <= C::NT, "one load per n-tile group");
         wait_vmcnt<C::kLoads>();
         barrier_nofence();
-        for (int ks = 0; ks < nk; ++ks) step8(ks);
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));  // lgkmcnt(0)
+    };
+    static_assert(C::kWaves == 8, "the K-step schedule assumes two waves per SIMD");
+    wait_vmcnt<0>();
+    issue(0, 0);
+    issue(min(1, nk - 1), 1);
+    wait_vmcnt<C::kLoads>();
+    barrier_nofence();
+    for (int ks = 0; ks < nk; ++ks) step8(ks);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));  // lgkmcnt(0)
 
-        // ---------------------------------------------------------------- epilogue
-        if (kG1) {
-            // lane holds, for row 4*lg + i of m-tile mt, the h columns
-            // icol0 + l16*(NT/2) + q, q < NT/2 (gate acc[2q], up acc[2q+1])
-            constexpr int QN = C::NT / 2;
-            const int icol0 = ntile * (BN / 2) + wn * (C::WTN / 2);
+    // ---------------------------------------------------------------- epilogue
+    if (kG1) {
+        // lane holds, for row 4*lg + i of m-tile mt, the h columns
+        // icol0 + l16*(NT/2) + q, q < NT/2 (gate acc[2q], up acc[2q+1])
+        constexpr int QN = C::NT / 2;
+        const int icol0 = ntile * (BN / 2) + wn * (C::WTN / 2);
 #pragma unroll
-            for (int mt = 0; mt < C::MT; ++mt) {
-                // one m-tile at a time: keeps the accumulators in AGPRs until used
-                __builtin_amdgcn_sched_barrier(0);
+        for (int mt = 0; mt < C::MT; ++mt) {
+            // one m-tile at a time: keeps the accumulators in AGPRs until used
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = wm * C::WTM + mt * 16 + 4 * lg + i;
-                    const float wr = s_w[r];
-                    float h[QN];
-                    float amax = 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int r = wm * C::WTM + mt * 16 + 4 * lg + i;
+                const float wr = s_w[r];
+                float h[QN];
+                float amax = 0.f;
 #pragma unroll
-                    for (int q = 0; q < QN; ++q) {
-                        float g = acc[mt][2 * q][i], u = acc[mt][2 * q + 1][i];
-                        h[q] = swiglu_w(g, u, wr);
-                        amax = fmaxf(amax, __builtin_fabsf(h[q]));
-                    }
-                    // a 32-column group spans 32 / QN neighbouring lanes of the 16
-#pragma unroll
-                    for (int o = 1; o < 32 / QN; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-                    const int ex = e4m3_block_exp(amax);
-                    const float inv = exp2_neg(ex);
-                    const int col = icol0 + l16 * QN;
-                    if (r < valid && col < p.I) {
-                        const int64_t pos = p0 + r;
-                        uint8_t* dst = p.hq + pos * p.I + col;
-                        static_assert(QN % 4 == 0, "whole dwords of E4M3 codes per lane");
-#pragma unroll
-                        for (int q = 0; q < QN; q += 4)
-                            *reinterpret_cast<uint32_t*>(dst + q) =
-                                e4m3_pack4(h[q] * inv, h[q + 1] * inv, h[q + 2] * inv, h[q + 3] * inv);
-                        if ((col & (kGroup - 1)) == 0)
-                            p.hsf[(int64_t)(col / (4 * kGroup)) * (p.T * p.topk) * 4 + pos * 4 +
-                                  (col / kGroup) % 4] = (uint8_t)(ex + 127);
-                    }
+                for (int q = 0; q < QN; ++q) {
+                    float g = acc[mt][2 * q][i], u = acc[mt][2 * q + 1][i];
+                    h[q] = swiglu_w(g, u, wr);
+                    amax = fmaxf(amax, __builtin_fabsf(h[q]));
                 }
-            }
-        } else {
-            // lane holds row 4*lg + i, output columns n0 + l16*NT + nt, nt < NT
-            const int n0 = ntile * BN + wn * C::WTN + l16 * C::NT;
+                // a 32-column group spans 32 / QN neighbouring lanes of the 16
 #pragma unroll
-            for (int mt = 0; mt < C::MT; ++mt) {
-                // one m-tile at a time: keeps the accumulators in AGPRs until used
-                __builtin_amdgcn_sched_barrier(0);
+                for (int o = 1; o < 32 / QN; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+                const int ex = e4m3_block_exp(amax);
+                const float inv = exp2_neg(ex);
+                const int col = icol0 + l16 * QN;
+                if (r < valid && col < p.I) {
+                    const int64_t pos = p0 + r;
+                    uint8_t* dst = p.hq + pos * p.I + col;
+                    static_assert(QN % 4 == 0, "whole dwords of E4M3 codes per lane");
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = wm * C::WTM + mt * 16 + 4 * lg + i;
-                    if (r < valid && n0 < p.H) {
-                        uint16_t* dst = p.o + (int64_t)(p0 + r) * p.H + n0;
-                        if constexpr (C::NT == 8) {
-                            uint4 v;
-                            v.x = f32_to_bf16(acc[mt][0][i]) | (f32_to_bf16(acc[mt][1][i]) << 16);
-                            v.y = f32_to_bf16(acc[mt][2][i]) | (f32_to_bf16(acc[mt][3][i]) << 16);
-                            v.z = f32_to_bf16(acc[mt][4][i]) | (f32_to_bf16(acc[mt][5][i]) << 16);
-                            v.w = f32_to_bf16(acc[mt][6][i]) | (f32_to_bf16(acc[mt][7][i]) << 16);
-                            *reinterpret_cast<uint4*>(dst) = v;
-                        } else {
-#pragma unroll
-                            for (int nt = 0; nt < C::NT; ++nt)
-                                dst[nt] = (uint16_t)f32_to_bf16(acc[mt][nt][i]);
-                        }
+                    for (int q = 0; q < QN; q += 4) {
+                        const uint32_t v = e4m3_pack4(h[q] * inv, h[q + 1] * inv, h[q + 2] * inv,
+                                                      h[q + 3] * inv);
+                        uint32_t* d = reinterpret_cast<uint32_t*>(dst + q);
+                        if constexpr (kCoh)
+                            __hip_atomic_store(d, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        else
+                            *d = v;
+                    }
+                    if ((col & (kGroup - 1)) == 0) {
+                        uint8_t* d = p.hsf + (int64_t)(col / (4 * kGroup)) * (p.T * p.topk) * 4 +
+                                     pos * 4 + (col / kGroup) % 4;
+                        if constexpr (kCoh)
+                            __hip_atomic_store(d, (uint8_t)(ex + 127), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                        else
+                            *d = (uint8_t)(ex + 127);
                     }
                 }
             }
         }
-        __syncthreads();
+    } else {
+        // lane holds row 4*lg + i, output columns n0 + l16*NT + nt, nt < NT
+        const int n0 = ntile * BN + wn * C::WTN + l16 * C::NT;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) {
+            // one m-tile at a time: keeps the accumulators in AGPRs until used
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wm * C::WTM + mt * 16 + 4 * lg + i;
+                if (r < valid && n0 < p.H) {
+                    uint16_t* dst = p.o + (int64_t)(p0 + r) * p.H + n0;
+                    if constexpr (C::NT == 8) {
+                        uint4 v;
+                        v.x = f32_to_bf16(acc[mt][0][i]) | (f32_to_bf16(acc[mt][1][i]) << 16);
+                        v.y = f32_to_bf16(acc[mt][2][i]) | (f32_to_bf16(acc[mt][3][i]) << 16);
+                        v.z = f32_to_bf16(acc[mt][4][i]) | (f32_to_bf16(acc[mt][5][i]) << 16);
+                        v.w = f32_to_bf16(acc[mt][6][i]) | (f32_to_bf16(acc[mt][7][i]) << 16);
+                        *reinterpret_cast<uint4*>(dst) = v;
+                    } else {
+#pragma unroll
+                        for (int nt = 0; nt < C::NT; ++nt)
+                            dst[nt] = (uint16_t)f32_to_bf16(acc[mt][nt][i]);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// n-tiles of GEMM1 (BN/2 columns of I, gate and up) or GEMM2 (BN columns of
+// H); the last one may be partial (I and H are multiples of 128).
+template <int BN>
+MOE_DEV int gemm_ntiles(const GemmParams& p, bool g1) {
+    return g1 ? (p.I + BN / 2 - 1) / (BN / 2) : (p.H + BN - 1) / BN;
+}
+
+// Workgroup slot of this workgroup: consecutive for the workgroups of one XCD.
+MOE_DEV int xcd_slot() {
+    const int grid = gridDim.x;
+    return (grid % kXCDs) == 0 ? (blockIdx.x % kXCDs) * (grid / kXCDs) + blockIdx.x / kXCDs
+                               : blockIdx.x;
+}
+
+// Tile number t of a run of m-tiles [m0, m0 + nm) x nt n-tiles in the grouped
+// order: groups of kGM m-tiles x all n-tiles, m fastest inside a group.
+MOE_DEV void grouped_order(int t, int m0, int nm, int nt, int* mt, int* ntile) {
+    const int grp = t / (kGM * nt);
+    const int gm = min(kGM, nm - grp * kGM);
+    const int in_grp = t - grp * (kGM * nt);
+    *ntile = in_grp / gm;
+    *mt = m0 + grp * kGM + (in_grp - *ntile * gm);
+}
+
+// GEMM1 or GEMM2 alone (one launch each, ordered by the stream).
+template <int BM, int BN, int WM, int WN, bool kG1>
+__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParams p) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    __shared__ int s_tile[4];
+    const int NT = gemm_ntiles<BN>(p, kG1);
+    const int mtiles = p.mtile_off[p.E];
+    const int total = mtiles * NT;
+    for (int tile = xcd_slot(); tile < total; tile += gridDim.x) {
+        int mt, ntile;
+        grouped_order(tile, 0, mtiles, NT, &mt, &ntile);
+        gemm_tile<BM, BN, WM, WN, kG1, false>(p, mt, ntile, smem, s_tile);
+    }
+}
+
+// GEMM1 -> SwiGLU -> GEMM2 in one persistent launch ("MegaMoE" notes,
+// "Scheduler" and "Wave"; "MegaMoE：把通信和计算融合到一个 Mega Kernel", wave-based
+// expert processing).  Experts are cut into waves of p.wave_experts; the tile
+// list is GEMM1(wave 0), GEMM1(wave 1), GEMM2(wave 0), GEMM1(wave 2),
+// GEMM2(wave 1), ..., GEMM2(last wave), each run in the grouped order, and
+// workgroup slot q takes list entries q, q + grid, ... .  A GEMM1 tile adds one
+// to ready[m] once its h columns are stored; a GEMM2 tile of m-tile m starts
+// when ready[m] counts every GEMM1 n-tile of m (the bucketing stage of the call
+// zeroes ready[] before this launch).  A GEMM2 entry only waits for GEMM1
+// entries earlier in the list and every workgroup is resident (one per CU),
+// so the waits always end; a wait longer than kSpinLimit polls stops, sets
+// *p.status and lets the tile run (its output is then wrong, never a hang).
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams p) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    __shared__ int s_tile[4];
+    const int tid = threadIdx.x;
+    const int NT1 = gemm_ntiles<BN>(p, true), NT2 = gemm_ntiles<BN>(p, false);
+    const int ew = p.wave_experts;
+    const int nw = (p.E + ew - 1) / ew;
+    const int nseg = 2 * nw;
+    // segment s of the list: GEMM1 of wave w = (s + 1) / 2 (s = 0 or odd),
+    // GEMM2 of wave w = s / 2 - 1 (s even > 0) and of the last wave (s = nseg - 1)
+    auto seg_of = [&](int sidx, int* g1, int* m0, int* nm) {
+        int w;
+        if (sidx == nseg - 1) { *g1 = 0; w = nw - 1; }
+        else if (sidx == 0 || (sidx & 1)) { *g1 = 1; w = (sidx + 1) / 2; }
+        else { *g1 = 0; w = sidx / 2 - 1; }
+        const int a = p.mtile_off[min(w * ew, p.E)], b = p.mtile_off[min((w + 1) * ew, p.E)];
+        *m0 = a;
+        *nm = b - a;
+    };
+    int seg = -1, seg_start = 0, seg_len = 0, g1 = 1, m0 = 0, nm = 0;
+    const int total = p.mtile_off[p.E] * (NT1 + NT2);
+    for (int tile = xcd_slot(); tile < total; tile += gridDim.x) {
+        while (tile >= seg_start + seg_len) {      // advance to the segment holding tile
+            seg_start += seg_len;
+            ++seg;
+            seg_of(seg, &g1, &m0, &nm);
+            seg_len = nm * (g1 ? NT1 : NT2);
+        }
+        int mt, ntile;
+        grouped_order(tile - seg_start, m0, nm, g1 ? NT1 : NT2, &mt, &ntile);
+        if (g1) {
+            gemm_tile<BM, BN, WM, WN, true, true>(p, mt, ntile, smem, s_tile);
+            // every thread's coherent h stores have completed (vmcnt(0)) before the barrier
+            __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8) | (0 << 14));
+            __syncthreads();
+            if (tid == 0)
+                __hip_atomic_fetch_add(p.ready + mt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            if (tid == 0) {
+                int n = 0;
+                while (__hip_atomic_load(p.ready + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                       NT1) {
+                    __builtin_amdgcn_s_sleep(1);
+                    if (++n > kSpinLimit) {
+                        __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                }
+            }
+            __syncthreads();
+            gemm_tile<BM, BN, WM, WN, false, true>(p, mt, ntile, smem, s_tile);
+        }
     }
 }
 
@@ -449,23 +557,31 @@ constexpr int kBM = 128, kBN = 512, kWM = 2, kWN = 4;
 
 int gemm_bm() { return kBM; }
 
+static int device_cus() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+    }
+    return cus;
+}
+
 template <bool kG1>
 static hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     using C = Cfg<kBM, kBN, kWM, kWN, kG1>;
     auto kern = grouped_gemm_kernel<kBM, kBN, kWM, kWN, kG1>;
     const size_t lds = C::kStages * (size_t)C::kStage + (size_t)kBM * 8;
     static bool attr_set = false;
-    static int cus = 0;
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute((const void*)kern,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        int dev = 0;
-        if (err == hipSuccess) err = hipGetDevice(&dev);
-        if (err == hipSuccess)
-            err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (err != hipSuccess) return err;
         attr_set = true;
     }
+    const int cus = device_cus();
+    if (cus <= 0) return hipErrorInvalidDevice;
     const int ntiles = kG1 ? (p.I + kBN / 2 - 1) / (kBN / 2) : (p.H + kBN - 1) / kBN;
     const int64_t upper = (int64_t)p.max_mtiles * ntiles;
     const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(upper, cus));
@@ -475,5 +591,35 @@ static hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
 
 hipError_t launch_gemm1(const GemmParams& p, hipStream_t s) { return launch_gemm<true>(p, s); }
 hipError_t launch_gemm2(const GemmParams& p, hipStream_t s) { return launch_gemm<false>(p, s); }
+
+hipError_t launch_fused_gemm(const GemmParams& p_in, hipStream_t s) {
+    using C = Cfg<kBM, kBN, kWM, kWN, true>;
+    auto kern = fused_gemm_kernel<kBM, kBN, kWM, kWN>;
+    const size_t lds = C::kStages * (size_t)C::kStage + (size_t)kBM * 8;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (err != hipSuccess) return err;
+        attr_set = true;
+    }
+    const int cus = device_cus();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    GemmParams p = p_in;
+    // experts per wave: enough GEMM1 tiles to give every CU about two
+    // ("MegaMoE" notes, "Wave": ceil(2 * SMs / L1 blocks per expert))
+    const int64_t R = p.T * p.topk;
+    const int nt1 = (p.I + kBN / 2 - 1) / (kBN / 2), nt2 = (p.H + kBN - 1) / kBN;
+    const int64_t rows_per_expert = std::max<int64_t>(1, (R + p.E - 1) / p.E);
+    const int64_t tiles_per_expert = (rows_per_expert + kBM - 1) / kBM * nt1;
+    p.wave_experts = (int)std::min<int64_t>(
+        p.E, std::max<int64_t>(1, (2 * (int64_t)cus + tiles_per_expert - 1) / tiles_per_expert));
+    // one workgroup per CU, all resident at once: a GEMM2 tile may wait for a GEMM1
+    // tile of any other workgroup
+    const int64_t upper = (int64_t)p.max_mtiles * (nt1 + nt2);
+    const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(upper, cus));
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), lds, s, p);
+    return hipGetLastError();
+}
 
 }  // namespace moe

@@ -10,6 +10,7 @@ namespace moe {
 
 constexpr int kRouteTokensPerBlock = 16;
 constexpr int kSubRows = 16;            // rows of a sub-tile (the narrow GEMMs' unit of rows)
+constexpr int kMaxExpertsCap = 1024;    // largest E the library takes
 
 struct RouteParams {
     const float* logits;        // [T, E] or null
@@ -39,6 +40,8 @@ struct ScatterParams {
                                 // past the last m-tile
     int4* sub_rec;              // [max_subs] the same for 16-row sub-tiles
     int32_t* nsub;              // [1] number of 16-row sub-tiles
+    int* ready;                 // [max_mtiles] zeroed here for the one-launch GEMMs
+    int* status;                // [1] zeroed here
     int32_t* slot_src;          // [T*k]
     int32_t* slot_of;           // [T, k]
     int64_t T;
@@ -78,11 +81,17 @@ struct GemmParams {
     int H, I, E, topk;
     int max_mtiles;             // upper bound of mtile_off[E]
     int max_subs;               // upper bound of *nsub
+    // one-launch GEMM1 -> GEMM2 (both zeroed by the bucketing stage of the call)
+    int* ready;                 // [max_mtiles] GEMM1 n-tiles of the m-tile whose h is stored
+    int* status;                // [1] set to 1 if a wait gave up (never in a correct run)
+    int wave_experts;           // experts per scheduling wave (set by the launcher)
 };
 
 int gemm_bm();                  // rows per m-tile of the grouped GEMMs
 hipError_t launch_gemm1(const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm2(const GemmParams& p, hipStream_t s);
+// GEMM1 -> SwiGLU -> GEMM2 in one persistent launch with per-m-tile ready counters
+hipError_t launch_fused_gemm(const GemmParams& p, hipStream_t s);
 // the same two GEMMs for few rows per expert (decode): N split over many small
 // workgroups that stream weights straight into registers
 hipError_t launch_narrow_gemm1(const GemmParams& p, hipStream_t s);

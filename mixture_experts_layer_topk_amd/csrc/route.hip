@@ -26,7 +26,7 @@ namespace moe {
 constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kMaxTopk = 16;
-constexpr int kMaxExperts = 1024;
+constexpr int kMaxExperts = kMaxExpertsCap;
 constexpr int kSmallPairs = 1024;       // T * k up to which one workgroup buckets every pair
 
 // Unsigned integer with the order of the float value (finite inputs); -0 and
@@ -279,6 +279,9 @@ MOE_DEV void write_tables(const ScatterParams& p, const int* cnt, const int* off
     const int tid = threadIdx.x;
     for (int e = tid; e < p.E; e += kRouteThreads) p.counts_out[e] = cnt[e];
     for (int e = tid; e <= p.E; e += kRouteThreads) p.offsets_out[e] = off[e];
+    // the one-launch GEMMs' per-m-tile counters and status start at zero
+    for (int m = tid; m < p.max_mtiles; m += kRouteThreads) p.ready[m] = 0;
+    if (tid == 0) *p.status = 0;
     for (int pass = 0; pass < 2; ++pass) {
         const int rows = pass == 0 ? p.bm : kSubRows;
         const int cap = pass == 0 ? p.max_mtiles : p.max_subs;

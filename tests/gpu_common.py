@@ -110,6 +110,8 @@ class DeviceLayer:
             y = m.forward(self.d, self.x, self.w13q, self.w13sf_k, self.w2q, self.w2sf_k, self.ws,
                           logits=self.logits, flags=flags)
         torch.cuda.synchronize()
+        status = int(m.intermediates(self.d, self.ws)["status"].item())
+        assert status == 0, "a GEMM2 tile gave up waiting for its GEMM1 tiles"
         return y
 
     def intermediates(self):

@@ -236,8 +236,8 @@ AGREE_SHAPES = [W.WORKLOADS["decode"], W.WORKLOADS["tiny"], RAGGED,
 
 @pytest.mark.parametrize("w", AGREE_SHAPES, ids=lambda w: w.name)
 def test_narrow_and_tiled_gemms_match_oracle(w):
-    """Both GEMM kernel families, forced on the same inputs, against the oracle (the
-    default picks one family per shape; this runs the other one too)."""
+    """Every GEMM path (narrow; tiled in one launch; tiled in two launches), forced on
+    the same inputs, against the oracle (the default picks one per shape)."""
     m = G.lib()
     _log(f"narrow and tiled {w.name}")
     ext = None
@@ -246,7 +246,8 @@ def test_narrow_and_tiled_gemms_match_oracle(w):
     dl = G.DeviceLayer(w, external_topk=ext)
     ref = _oracle_full(w, ext)
     so_r = ref["slot_of"].reshape(-1)
-    for name, flag in (("narrow", m.FLAG_NARROW), ("tiled", m.FLAG_TILED)):
+    for name, flag in (("narrow", m.FLAG_NARROW), ("tiled, two launches", m.FLAG_TILED),
+                       ("tiled, one launch", m.FLAG_ONE_LAUNCH)):
         _log(f"  {name}")
         y = dl.forward(use_logits=ext is None, flags=flag)
         inter = dl.intermediates()
@@ -254,6 +255,21 @@ def test_narrow_and_tiled_gemms_match_oracle(w):
         ok = so_r >= 0
         G.check_hq(inter["hq"][so_g[ok]], inter["hsf"][so_g[ok]], ref["hq"][so_r[ok]],
                    ref["hsf"][so_r[ok]])
+        G.check_y(G.y_bits(y), ref["y"])
+
+
+def test_one_launch_reads_this_calls_h():
+    """Alternating two different inputs on one workspace: a GEMM2 tile that read h
+    left in a cache by the previous call (instead of this call's GEMM1 tiles) would
+    give the other input's result."""
+    m = G.lib()
+    wa, wb = RAGGED, W.Workload("ragged_b", T=601, H=640, I=384, E=5, topk=2, seed=1)
+    _log("one launch, alternating inputs")
+    da, db = G.DeviceLayer(wa), G.DeviceLayer(wb)
+    db.ws = da.ws
+    ra, rb = _oracle_full(wa), _oracle_full(wb)
+    for dl, ref in ((da, ra), (db, rb), (da, ra), (db, rb)):
+        y = dl.forward(flags=m.FLAG_ONE_LAUNCH)
         G.check_y(G.y_bits(y), ref["y"])
 
 
