@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_prefill")
-    ap.add_argument("--cpu-sample-experts", type=int, default=1,
+    ap.add_argument("--cpu-sample-experts", type=int, default=24,
                     help="experts whose rows the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gemm-path", choices=("auto", "narrow", "tiled", "one-launch"),
