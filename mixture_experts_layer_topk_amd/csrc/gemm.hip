@@ -49,7 +49,11 @@
 // the XOR swizzle of the LDS tiles is applied on the global side by choosing
 // which 16-byte chunk each lane fetches.  Three LDS stages rotate: the loads
 // of step ks + 2 are issued during step ks into the stage every wave retired
-// at the barrier that ended step ks - 1.
+// at the barrier that ended step ks - 1.  In the two-launch kernels the ring
+// runs on from one tile of a workgroup to its next: the last two K steps of a
+// tile load the next tile's first two, whose row tables and load sources were
+// set up during the K loop, so a tile's epilogue overlaps the next tile's
+// first loads instead of a drained pipeline.
 //
 // Eight waves, two per SIMD, each 64 x 128 of the tile.  The SIMD's two waves
 // are de-phased (wm = 0 early, wm = 1 late): after the barrier that publishes
@@ -85,19 +89,27 @@ struct Cfg {
     static constexpr int kSBBytes = BN * 4;
     static constexpr int kStage = kABytes + kBBytes + kSABytes + kSBBytes;
     static constexpr int kStages = 3;
+    // LDS: the stages, then two tiles' token rows and topk weights and one
+    // staging row of pair indices
+    static constexpr int kRowBytes = BM * (2 * 4 + 2 * 4 + 4);
+    static constexpr int kLds = kStages * kStage + kRowBytes;
     static constexpr int kAI = kABytes / 1024 / kWaves;   // 1 KiB load instructions per wave
     static constexpr int kBI = kBBytes / 1024 / kWaves;
-    // scale tiles: one dword per lane, 64 rows per load; when a tile has fewer
-    // than 64 * kWaves rows the waves repeat each other's loads (same bytes to
-    // the same LDS address), so every wave issues the same number of loads
-    static constexpr int kSAI = (kSABytes + 256 * kWaves - 1) / (256 * kWaves);
-    static constexpr int kSBI = (kSBBytes + 256 * kWaves - 1) / (256 * kWaves);
-    static constexpr int kSARows = BM, kSBRows = BN;
-    static constexpr int kLoads = kAI + kBI + kSAI + kSBI;  // per thread per stage
+    // Scale tiles: one dword per lane, 64 rows per load, issued by the early
+    // waves only (wm = 0, waves 0 .. kEarly - 1), whose loads are off the
+    // step's critical path: early wave e loads B-scale blocks kSBE e ..
+    // kSBE e + kSBE - 1 and, if e < kSABlocks, A-scale block e.
+    static constexpr int kEarly = WN;
+    static constexpr int kSABlocks = BM / 64, kSBBlocks = BN / 64;
+    static constexpr int kSBE = kSBBlocks / kEarly;
+    static constexpr int kLoadsLate = kAI + kBI;            // per wave per stage
+    static constexpr int kLoadsEarly = kAI + kBI + kSBE;    // + 1 with an A-scale block
     static_assert(kABytes % (1024 * kWaves) == 0 && kBBytes % (1024 * kWaves) == 0, "tile / waves");
     static_assert(BM % 64 == 0 && BN % 64 == 0, "scale tiles in whole 64-row loads");
     static_assert(MT >= 1 && NT >= 2 && NT % 2 == 0, "wave tile");
-    static_assert(kLoads < 64, "vmcnt range");
+    static_assert(WM == 2 && kSBBlocks % kEarly == 0 && kSABlocks <= kEarly, "scale loads");
+    static_assert(kLoadsEarly + 1 < 64, "vmcnt range");
+    static_assert(kLds <= 160 * 1024, "LDS of one CU");
 };
 
 // LDS swizzles.  An A fragment read touches 16 consecutive rows (128 bytes
@@ -153,314 +165,431 @@ MOE_DEV void load_lds4(const void* g, uint8_t* lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 4, 0, kAux);
 }
 
-// One BM x BN output tile of GEMM1 (kG1) or GEMM2 over all of K, epilogue
-// included.  kCoh: the tile runs inside the one-launch kernel, where GEMM2 reads
-// h that other XCDs wrote in the same launch; h is then stored and read with
+// Per-workgroup GEMM state for one output tile at a time: the per-lane global
+// sources of the load instructions, the MFMA operands and the accumulators,
+// with the pieces of the K-step schedule as members so that the grouped
+// kernels (tiles back to back, next tile prefetched) and the one-launch kernel
+// (one tile at a time) run the same code.
+//
+// LDS: kStages stages, then the row tables of two tiles (the one in the K loop
+// and the next one): token row per A row (GEMM1), topk weight per A row, and
+// a staging row for the position -> pair lookup of the next tile.
+// kCoh: the tile runs inside the one-launch kernel, where GEMM2 reads h that
+// other XCDs wrote in the same launch; h is then stored and read with
 // device-coherent accesses (sc1), which go to the memory-side cache instead of
 // an XCD's own L2, while the weights keep the cached path.
 template <int BM, int BN, int WM, int WN, bool kG1, bool kCoh>
-MOE_DEV void gemm_tile(const GemmParams& p, int mt_g, int ntile, uint8_t* smem, int* s_tile) {
+struct TileEngine {
     using C = Cfg<BM, BN, WM, WN, kG1>;
-    constexpr int kAuxA = (kCoh && !kG1) ? kCohAux : 0;
-    int* s_tok = reinterpret_cast<int*>(smem + C::kStages * C::kStage);   // [BM] A row source
-    float* s_w = reinterpret_cast<float*>(s_tok + BM);                     // [BM] topk weight
-    const int tid = threadIdx.x;
-    const int K = kG1 ? p.H : p.I;                 // reduction length
-    const int nk = K / BK;
-    // Scales are stored K-step major: the 4 UE8M0 bytes of one 128-wide K step
-    // for row r sit at slab[ks][r][0..3], so a tile's scales for one K step are
-    // 4-byte entries of one slab rather than bytes strided across the rows.
-    const int64_t sa_slab = 4 * (kG1 ? p.T : p.T * p.topk);   // activation rows per slab
-    const int64_t sb_slab = 4 * (int64_t)(kG1 ? 2 * p.I : p.H); // weight rows per slab
-    const uint8_t* a_base = kG1 ? p.xq : p.hq;
-    const uint8_t* sa_base = kG1 ? p.xsf : p.hsf;
+    static constexpr int kAuxA = (kCoh && !kG1) ? kCohAux : 0;
 
-    // Per-lane indices are re-derived from an opaque copy of the thread id in
-    // every tile, so the compiler recomputes the (cheap) per-lane constants
-    // here instead of keeping dozens of them alive across the K loop.
-    int tid_v = tid;
-    asm volatile("" : "+v"(tid_v));
-    const int lane = tid_v & 63;
-    const int wave = tid_v >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const int l16 = lane & 15, lg = lane >> 4;
-    if (tid == 0) {
-        const int4 rec = p.mtile_rec[mt_g];      // {expert, first position, rows}
-        s_tile[0] = rec.x;
-        s_tile[1] = rec.y;
-        s_tile[2] = rec.z;
-    }
-    __syncthreads();
-    const int e = s_tile[0];
-    const int p0 = s_tile[1];
-    const int valid = s_tile[2];
+    const GemmParams& p;
+    uint8_t* smem;
+    int* s_tok;         // [2][BM] A row source (token row), GEMM1
+    float* s_w;         // [2][BM] topk weight of the A row, GEMM1
+    int* s_pair;        // [BM]    pair index of the A row, staging for the next tile
+    int K, nk;          // reduction length and K steps
+    int64_t sa_slab, sb_slab;
+    const uint8_t* a_base;
+    const uint8_t* sa_base;
+    // sources of the next K step to load (A, B, A scales, B scales), advanced
+    // by one K step per issue
+    const uint8_t* ld_a;
+    const uint8_t* ld_w;
+    const uint8_t* ld_sa;
+    const uint8_t* ld_sw;
+    bool late;                  // the second wave of this SIMD (wm == 1)
+    bool sa_wave;               // an early wave that loads an A-scale block
+    int lg;
+    int a_lo, a_hi, b_fr, sa_fr, sb_fr;
 
-    // row sources of the A tile: token rows (GEMM1) or positions (GEMM2)
-    if (tid < BM) {
-        int pr = p0 + min(tid, valid - 1);
-        if (kG1) {
-            int src = p.slot_src[pr];
-            s_tok[tid] = src / p.topk;
-            s_w[tid] = p.topk_w[src];
-        } else {
-            s_tok[tid] = pr;
-        }
-    }
-    __syncthreads();
+    uint32_t a_src[C::kAI];
+    uint32_t b_src[C::kBI];
+    uint32_t sa_src;
+    uint32_t sb_src[C::kSBE];
+    v4f acc[C::MT][C::NT];
+    v8i a[C::MT];
+    v4i b[C::NT];
+    // scale dwords as read: byte lg of dword t of run h is the scale of K group
+    // lg for tile 4h + t; the byte is extracted where the MFMAs use it, so
+    // nothing between the fragment reads and the load issue waits for LDS
+    v4i sa_run[C::MT / 4];
+    v4i sb_run[C::NT / 4];
 
-    // B tile LDS row -> weight row.  Inside a wave's slice, LDS row nt*16 + c
-    // holds output column c*NT + nt (GEMM2) or, for GEMM1, I column
-    // c*NT/2 + nt/2 of the gate (even nt) or up (odd nt) projection.
-    auto b_row = [&](int b) -> int {
-        int ws = b / C::WTN, bl = b % C::WTN;
-        int nt = bl >> 4, c = bl & 15;
-        if (kG1) {
-            int icol = ntile * (BN / 2) + ws * (C::WTN / 2) + c * (C::NT / 2) + (nt >> 1);
-            icol = min(icol, p.I - 1);          // partial last n-tile: never stored
-            return (nt & 1) ? p.I + icol : icol;
-        } else {
-            int n = ntile * BN + ws * C::WTN + c * C::NT + nt;
-            return min(n, p.H - 1);
+    // Per-lane indices are re-derived from an opaque copy of the thread id
+    // where they are needed, so the compiler recomputes the (cheap) per-lane
+    // constants instead of keeping dozens of them alive across the K loop.
+    struct Lane {
+        int tid, lane, wave, wm, wn, l16, lg;
+        __device__ __forceinline__ Lane() {
+            int t = threadIdx.x;
+            asm volatile("" : "+v"(t));
+            tid = t;
+            lane = t & 63;
+            wave = t >> 6;
+            wm = wave / WN;
+            wn = wave % WN;
+            l16 = lane & 15;
+            lg = lane >> 4;
         }
     };
-    const int64_t b_stride = K / 2;
-    const uint8_t* w_base = kG1 ? p.w13 + (int64_t)e * (2 * p.I) * b_stride
-                                : p.w2 + (int64_t)e * p.H * b_stride;
-    const uint8_t* wsf_base = (kG1 ? p.w13sf : p.w2sf) + (int64_t)e * nk * sb_slab;
 
-    // per-lane global sources of each load instruction (fixed over K), as
-    // 32-bit byte offsets from wave-uniform bases
-    uint32_t a_src[C::kAI];
-#pragma unroll
-    for (int j = 0; j < C::kAI; ++j) {
-        int r = 8 * (j * C::kWaves + wave) + (lane >> 3);
-        int c = (lane & 7) ^ a_swz(r);
-        a_src[j] = (uint32_t)s_tok[r] * (uint32_t)K + c * 16;
+    __device__ __forceinline__ TileEngine(const GemmParams& pp, uint8_t* sm) : p(pp), smem(sm) {
+        s_tok = reinterpret_cast<int*>(smem + C::kStages * C::kStage);
+        s_w = reinterpret_cast<float*>(s_tok + 2 * BM);
+        s_pair = reinterpret_cast<int*>(s_w + 2 * BM);
+        K = kG1 ? p.H : p.I;
+        nk = K / BK;
+        // Scales are stored K-step major: the 4 UE8M0 bytes of one 128-wide K
+        // step for row r sit at slab[ks][r][0..3], so a tile's scales for one K
+        // step are 4-byte entries of one slab rather than bytes strided across rows.
+        sa_slab = 4 * (kG1 ? p.T : p.T * p.topk);
+        sb_slab = 4 * (int64_t)(kG1 ? 2 * p.I : p.H);
+        a_base = kG1 ? p.xq : p.hq;
+        sa_base = kG1 ? p.xsf : p.hsf;
+        const Lane L;
+        late = __builtin_amdgcn_readfirstlane(L.wm) == 1;
+        sa_wave = !late && __builtin_amdgcn_readfirstlane(L.wave) < C::kSABlocks;
+        lg = L.lg;
+        // MFMA operands.  Fragment addresses of different tiles differ by
+        // constants (the swizzles depend on row % 16 only).
+        const int a_row0 = L.wm * C::WTM + L.l16;
+        const int b_row0 = L.wn * C::WTN + L.l16;
+        a_lo = a_off(a_row0, L.lg);
+        a_hi = a_off(a_row0, 4 + L.lg);
+        b_fr = C::kABytes + b_off(b_row0, L.lg);
+        // scale runs of this lane: tiles 4h .. 4h+3 at slot base + 64 h + 4 l16
+        sa_fr = C::kABytes + C::kBBytes + 4 * (L.wm * C::WTM + 4 * L.l16);
+        sb_fr = C::kABytes + C::kBBytes + C::kSABytes + 4 * (L.wn * C::WTN + 4 * L.l16);
     }
-    uint32_t b_src[C::kBI];
-#pragma unroll
-    for (int j = 0; j < C::kBI; ++j) {
-        int n = 16 * (j * C::kWaves + wave) + (lane >> 2);
-        int c = (lane & 3) ^ b_swz(n);
-        b_src[j] = (uint32_t)b_row(n) * (uint32_t)b_stride + c * 16;
-    }
-    // 64-row block of scale load j of this wave (wrapping when the tile is short)
-    auto sa_blk = [&](int j) { return (j * C::kWaves + wave) % (C::kSARows / 64); };
-    auto sb_blk = [&](int j) { return (j * C::kWaves + wave) % (C::kSBRows / 64); };
-    uint32_t sa_src[C::kSAI];
-#pragma unroll
-    for (int j = 0; j < C::kSAI; ++j)
-        sa_src[j] = (uint32_t)s_tok[scale_slot_row(64 * sa_blk(j) + lane)] * 4u;
-    // B scales are staged in the B tile's LDS row order, regrouped by
-    // scale_slot_row: the slots of LDS row q hold weight row b_row(q).
-    uint32_t sb_src[C::kSBI];
-#pragma unroll
-    for (int j = 0; j < C::kSBI; ++j)
-        sb_src[j] = (uint32_t)b_row(scale_slot_row(64 * sb_blk(j) + lane)) * 4u;
 
-    // Load instruction j (of kLoads) of K slice ks into LDS stage `stage`:
-    // A tile chunks first, then B, then the two scale tiles.
-    auto issue_one = [&](int j, int ks, int stage) {
-        uint8_t* sA = smem + stage * C::kStage;
+    // Row tables of a GEMM1 tile {expert, first position, rows} into buffer
+    // buf, loaded and published at once (first tile, one-launch tiles).
+    __device__ __forceinline__ void load_rows_now(int4 rec, int buf) {
+        const int tid = threadIdx.x;
+        if (kG1 && tid < BM) {
+            const int pair = p.slot_src[rec.y + min(tid, rec.z - 1)];
+            s_tok[buf * BM + tid] = pair / p.topk;
+            s_w[buf * BM + tid] = p.topk_w[pair];
+        }
+        __syncthreads();
+    }
+    // The same for the next tile, spread over two K steps of the current one
+    // as loads straight into LDS: part 0 fetches the pair index of every row,
+    // part 1 (a step later, after the wait that retires part 0) derives the
+    // token row and fetches the topk weight.  Each part is issued before the
+    // step's tile loads, so the step's closing vmcnt wait retires it.
+    __device__ __forceinline__ void fetch_rows(int4 rec, int buf, int part) {
+        const Lane L;
+        if (!kG1 || L.wave * 64 >= BM) return;
+        if (part == 0) {
+            const int* src = p.slot_src + rec.y + min(L.tid, rec.z - 1);
+            load_lds4<0>(src, reinterpret_cast<uint8_t*>(s_pair + 64 * L.wave));
+        } else {
+            const int pair = s_pair[L.tid];
+            s_tok[buf * BM + L.tid] = pair / p.topk;
+            load_lds4<0>(p.topk_w + pair, reinterpret_cast<uint8_t*>(s_w + buf * BM + 64 * L.wave));
+        }
+    }
+
+    // Global sources of the loads of tile {rec, ntile}; for GEMM1 the token
+    // rows come from row buffer buf, which must be published.
+    __device__ __forceinline__ void set_tile(int4 rec, int ntile, int buf) {
+        const Lane L;
+        const int e = rec.x, p0 = rec.y, valid = rec.z;
+        auto row_src = [&](int r) -> uint32_t {
+            return kG1 ? (uint32_t)s_tok[buf * BM + r] : (uint32_t)(p0 + min(r, valid - 1));
+        };
+        // B tile LDS row -> weight row.  Inside a wave's slice, LDS row nt*16 + c
+        // holds output column c*NT + nt (GEMM2) or, for GEMM1, I column
+        // c*NT/2 + nt/2 of the gate (even nt) or up (odd nt) projection.
+        auto b_row = [&](int bq) -> uint32_t {
+            const int ws = bq / C::WTN, bl = bq % C::WTN;
+            const int nt = bl >> 4, c = bl & 15;
+            if (kG1) {
+                int icol = ntile * (BN / 2) + ws * (C::WTN / 2) + c * (C::NT / 2) + (nt >> 1);
+                icol = min(icol, p.I - 1);          // partial last n-tile: never stored
+                return (nt & 1) ? p.I + icol : icol;
+            } else {
+                const int n = ntile * BN + ws * C::WTN + c * C::NT + nt;
+                return min(n, p.H - 1);
+            }
+        };
+        const int64_t b_stride = K / 2;
+        ld_a = a_base;
+        ld_w = kG1 ? p.w13 + (int64_t)e * (2 * p.I) * b_stride : p.w2 + (int64_t)e * p.H * b_stride;
+        ld_sa = sa_base;
+        ld_sw = (kG1 ? p.w13sf : p.w2sf) + (int64_t)e * nk * sb_slab;
+        // per-lane global sources of each load instruction (fixed over K), as
+        // 32-bit byte offsets from wave-uniform bases
+#pragma unroll
+        for (int j = 0; j < C::kAI; ++j) {
+            const int r = 8 * (j * C::kWaves + L.wave) + (L.lane >> 3);
+            const int c = (L.lane & 7) ^ a_swz(r);
+            a_src[j] = row_src(r) * (uint32_t)K + c * 16;
+        }
+#pragma unroll
+        for (int j = 0; j < C::kBI; ++j) {
+            const int n = 16 * (j * C::kWaves + L.wave) + (L.lane >> 2);
+            const int c = (L.lane & 3) ^ b_swz(n);
+            b_src[j] = b_row(n) * (uint32_t)b_stride + c * 16;
+        }
+        // scale blocks of an early wave (a late wave's values are not used)
+        const int ew = L.wave % C::kEarly;
+        sa_src = row_src(scale_slot_row(64 * (ew % C::kSABlocks) + L.lane)) * 4u;
+        // B scales are staged in the B tile's LDS row order, regrouped by
+        // scale_slot_row: the slots of LDS row q hold weight row b_row(q).
+#pragma unroll
+        for (int j = 0; j < C::kSBE; ++j)
+            sb_src[j] = b_row(scale_slot_row(64 * (C::kSBE * ew + j) + L.lane)) * 4u;
+    }
+
+    __device__ __forceinline__ uint8_t* stage_ptr(int stage) const { return smem + stage * C::kStage; }
+
+    // The loads of the next K step into LDS stage `stage`: A tile chunks
+    // first, then B, then the two scale tiles.  The LDS destination (M0) is
+    // derived from a vector copy of the wave index: measured faster here than
+    // the same arithmetic on the scalar unit, which all waves of the CU share.
+    __device__ __forceinline__ void issue(int stage) {
+        int tv = threadIdx.x;
+        asm volatile("" : "+v"(tv));
+        const int wave = tv >> 6;
+        uint8_t* sA = stage_ptr(stage);
         uint8_t* sB = sA + C::kABytes;
         uint8_t* sSA = sB + C::kBBytes;
         uint8_t* sSB = sSA + C::kSABytes;
-        if (j < C::kAI) {
-            load_lds16<kAuxA>(a_base + ks * BK + a_src[j], sA + (j * C::kWaves + wave) * 1024);
-        } else if (j < C::kAI + C::kBI) {
-            const int jb = j - C::kAI;
-            load_lds16<0>(w_base + ks * (BK / 2) + b_src[jb], sB + (jb * C::kWaves + wave) * 1024);
-        } else if (j < C::kAI + C::kBI + C::kSAI) {
-            const int js = j - C::kAI - C::kBI;
-            load_lds4<kAuxA>(sa_base + ks * sa_slab + sa_src[js], sSA + sa_blk(js) * 256);
-        } else {
-            const int js = j - C::kAI - C::kBI - C::kSAI;
-            load_lds4<0>(wsf_base + ks * sb_slab + sb_src[js], sSB + sb_blk(js) * 256);
+#pragma unroll
+        for (int j = 0; j < C::kAI; ++j)
+            load_lds16<kAuxA>(ld_a + a_src[j], sA + (j * C::kWaves + wave) * 1024);
+#pragma unroll
+        for (int j = 0; j < C::kBI; ++j)
+            load_lds16<0>(ld_w + b_src[j], sB + (j * C::kWaves + wave) * 1024);
+        if (!late) {
+            if (sa_wave) load_lds4<kAuxA>(ld_sa + sa_src, sSA + wave * 256);
+#pragma unroll
+            for (int j = 0; j < C::kSBE; ++j)
+                load_lds4<0>(ld_sw + sb_src[j], sSB + (C::kSBE * wave + j) * 256);
         }
-    };
-    auto issue = [&](int ks, int stage) {   // K slice ks into LDS stage
-#pragma unroll
-        for (int j = 0; j < C::kLoads; ++j) issue_one(j, ks, stage);
-    };
+        ld_a += BK;
+        ld_w += BK / 2;
+        ld_sa += sa_slab;
+        ld_sw += sb_slab;
+    }
 
-    v4f acc[C::MT][C::NT];
+    __device__ __forceinline__ void zero_acc() {
 #pragma unroll
-    for (int i = 0; i < C::MT; ++i)
+        for (int i = 0; i < C::MT; ++i)
 #pragma unroll
-        for (int j = 0; j < C::NT; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < C::NT; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
 
-    // MFMA operands.  Fragment addresses of different tiles differ by
-    // constants (the swizzles depend on row % 16 only).
-    const int a_row0 = wm * C::WTM + l16;
-    const int b_row0 = wn * C::WTN + l16;
-    const int a_lo = a_off(a_row0, lg), a_hi = a_off(a_row0, 4 + lg);
-    const int b_fr = C::kABytes + b_off(b_row0, lg);
-    // scale runs of this lane: tiles 4h .. 4h+3 at slot base + 64 h + 4 l16
-    const int sa_fr = C::kABytes + C::kBBytes + 4 * (wm * C::WTM + 4 * l16);
-    const int sb_fr = C::kABytes + C::kBBytes + C::kSABytes + 4 * (wn * C::WTN + 4 * l16);
-    static_assert(C::MT % 4 == 0 && C::NT % 4 == 0, "scale runs of four tiles");
-    v8i a[C::MT];
-    int sa[C::MT];
-    v4i b[C::NT];
-    int sb[C::NT];
-    auto read_a = [&](const uint8_t* st, int mt) {
-        v4i lo = *reinterpret_cast<const v4i*>(st + a_lo + mt * 16 * BK);
-        v4i hi = *reinterpret_cast<const v4i*>(st + a_hi + mt * 16 * BK);
-        a[mt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    auto read_b = [&](const uint8_t* st, int nt) {
-        b[nt] = *reinterpret_cast<const v4i*>(st + b_fr + nt * 16 * (BK / 2));
-    };
+    __device__ __forceinline__ void read_frags(const uint8_t* st) {
+        static_assert(C::MT % 4 == 0 && C::NT % 4 == 0, "scale runs of four tiles");
+#pragma unroll
+        for (int h = 0; h < C::MT / 4; ++h) sa_run[h] = *reinterpret_cast<const v4i*>(st + sa_fr + 256 * h);
+#pragma unroll
+        for (int h = 0; h < C::NT / 4; ++h) sb_run[h] = *reinterpret_cast<const v4i*>(st + sb_fr + 256 * h);
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) {
+            const v4i lo = *reinterpret_cast<const v4i*>(st + a_lo + mt * 16 * BK);
+            const v4i hi = *reinterpret_cast<const v4i*>(st + a_hi + mt * 16 * BK);
+            a[mt] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt)
+            b[nt] = *reinterpret_cast<const v4i*>(st + b_fr + nt * 16 * (BK / 2));
+    }
     // lane group lg supplies the scale of K group lg: byte lg of each dword
-    auto read_scales = [&](const uint8_t* st) {
+    __device__ __forceinline__ void mfmas() {
+        int sa[C::MT], sb[C::NT];
 #pragma unroll
-        for (int h = 0; h < C::MT / 4; ++h) {
-            const v4i v = *reinterpret_cast<const v4i*>(st + sa_fr + 256 * h);
+        for (int mt = 0; mt < C::MT; ++mt) sa[mt] = (int)((uint32_t)sa_run[mt / 4][mt % 4] >> (8 * lg));
 #pragma unroll
-            for (int t = 0; t < 4; ++t) sa[4 * h + t] = (int)((uint32_t)v[t] >> (8 * lg));
-        }
-#pragma unroll
-        for (int h = 0; h < C::NT / 4; ++h) {
-            const v4i v = *reinterpret_cast<const v4i*>(st + sb_fr + 256 * h);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) sb[4 * h + t] = (int)((uint32_t)v[t] >> (8 * lg));
-        }
-    };
-    auto mma = [&](int mt, int nt) {
-        acc[mt][nt] = mfma_fp8_fp4(a[mt], b[nt], acc[mt][nt], sa[mt], sb[nt]);
-    };
-
-    // Two waves per SIMD (8 waves): the SIMD's other wave runs its MFMAs
-    // while this one waits on LDS, the barrier or the load queue, so one
-    // K step is simply: read step ks's A fragments, then per n-tile its B
-    // fragment, its four MFMAs and one load of step ks + 2 into the stage
-    // every wave has retired (spreading the load issue between the MFMAs
-    // measured 5% faster than issuing them all first), then wait for this
-    // wave's loads of step ks + 1 and barrier.
-    // the two waves of a SIMD (wm = 0 and wm = 1) are de-phased: after the
-    // barrier that publishes stage ks the early wave reads its fragments and
-    // then runs its MFMAs, the late wave first runs the MFMAs of step ks - 1
-    // (fragments already in registers) and then reads stage ks
-    const bool late = __builtin_amdgcn_readfirstlane(wm) == 1;
-    auto mfmas = [&]() {
+        for (int nt = 0; nt < C::NT; ++nt) sb[nt] = (int)((uint32_t)sb_run[nt / 4][nt % 4] >> (8 * lg));
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int mt = 0; mt < C::MT; ++mt) mma(mt, nt);
+            for (int mt = 0; mt < C::MT; ++mt)
+                acc[mt][nt] = mfma_fp8_fp4(a[mt], b[nt], acc[mt][nt], sa[mt], sb[nt]);
         }
         __builtin_amdgcn_sched_barrier(0);
-    };
-    auto step8 = [&](int ks) {
-        const uint8_t* cur = smem + (ks % C::kStages) * C::kStage;
-        const int ks2 = min(ks + 2, nk - 1), st2 = (ks + 2) % C::kStages;
-        if (late && ks > 0) mfmas();
-        read_scales(cur);
-#pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) read_a(cur, mt);
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) read_b(cur, nt);
+    }
+
+    // Steps 0 and 1 of the current tile into stages st and st + 1 (mod
+    // kStages) and publish step 0.
+    __device__ __forceinline__ void prologue(int st) {
+        static_assert(C::kWaves == 8, "the K-step schedule assumes two waves per SIMD");
+        wait_vmcnt<0>();
+        issue(st);
+        if (nk > 1) {
+            issue(next_stage(st));
+            wait_all_but_last_issue();
+        } else {
+            wait_vmcnt<0>();
+        }
+        barrier_nofence();
+    }
+    __device__ __forceinline__ static int next_stage(int st) { return st == C::kStages - 1 ? 0 : st + 1; }
+    // Retire every memory operation of this wave but the loads of its last issue().
+    __device__ __forceinline__ void wait_all_but_last_issue() const {
+        if (late)
+            wait_vmcnt<C::kLoadsLate>();
+        else if (sa_wave)
+            wait_vmcnt<C::kLoadsEarly + 1>();
+        else
+            wait_vmcnt<C::kLoadsEarly>();
+    }
+
+    // One K step on stage `cur`.  The two waves of a SIMD (wm = 0 and wm = 1)
+    // are de-phased: after the barrier that publishes the stage the early wave
+    // reads its fragments and then runs its MFMAs, the late wave first runs the
+    // MFMAs of the previous step (fragments already in registers) and then
+    // reads the stage, so one wave's LDS reads overlap the other's MFMAs.  The
+    // late wave runs its MFMAs at raised priority: when the early wave gets to
+    // its own MFMAs first, the late wave's still win the SIMD, so it can go on
+    // to its reads and loads while the early wave computes (without this the
+    // two waves' MFMAs interleave and the late wave's reads and loads end up
+    // after every MFMA of the step, with the matrix core idle).
+    // `loads()` issues this step's loads (step + 2, or one of the next tile's
+    // first two) and returns whether it issued any; `extra()` issues whatever
+    // must be retired by this step's wait.  The wait retires everything but
+    // this step's loads.
+    template <class Extra, class Loads>
+    __device__ __forceinline__ void step(const uint8_t* cur, bool first, Extra&& extra, Loads&& loads) {
+        if (late && !first) {
+            __builtin_amdgcn_s_setprio(2);
+            mfmas();
+            __builtin_amdgcn_s_setprio(0);
+        }
+        read_frags(cur);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < C::kLoads; ++j) issue_one(j, ks2, st2);
+        extra();
+        const bool issued = loads();
         __builtin_amdgcn_sched_barrier(0);
         if (!late) mfmas();
-        wait_vmcnt<C::kLoads>();
+        if (issued)
+            wait_all_but_last_issue();
+        else
+            wait_vmcnt<0>();
         barrier_nofence();
-    };
-    static_assert(C::kWaves == 8, "the K-step schedule assumes two waves per SIMD");
-    wait_vmcnt<0>();
-    issue(0, 0);
-    issue(min(1, nk - 1), 1);
-    wait_vmcnt<C::kLoads>();
-    barrier_nofence();
-    for (int ks = 0; ks < nk; ++ks) step8(ks);
-    if (late) mfmas();
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));  // lgkmcnt(0)
+    }
 
-    // ---------------------------------------------------------------- epilogue
-    if (kG1) {
-        // lane holds, for row 4*lg + i of m-tile mt, the h columns
-        // icol0 + l16*(NT/2) + q, q < NT/2 (gate acc[2q], up acc[2q+1])
-        constexpr int QN = C::NT / 2;
-        const int icol0 = ntile * (BN / 2) + wn * (C::WTN / 2);
+    // The late wave's last MFMAs.
+    __device__ __forceinline__ void finish() {
+        if (late) mfmas();
+        __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));  // lgkmcnt(0)
+    }
+
+    // ------------------------------------------------------------ epilogue
+    __device__ __forceinline__ void epilogue(int4 rec, int ntile, int buf) {
+        const Lane L;
+        const int p0 = rec.y, valid = rec.z;
+        if (kG1) {
+            // lane holds, for row 4*lg + i of m-tile mt, the h columns
+            // icol0 + l16*(NT/2) + q, q < NT/2 (gate acc[2q], up acc[2q+1])
+            constexpr int QN = C::NT / 2;
+            const int icol0 = ntile * (BN / 2) + L.wn * (C::WTN / 2);
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) {
-            // one m-tile at a time: keeps the accumulators in AGPRs until used
-            __builtin_amdgcn_sched_barrier(0);
+            for (int mt = 0; mt < C::MT; ++mt) {
+                // one m-tile at a time: keeps the accumulators in AGPRs until used
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wm * C::WTM + mt * 16 + 4 * lg + i;
-                const float wr = s_w[r];
-                float h[QN];
-                float amax = 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    const int r = L.wm * C::WTM + mt * 16 + 4 * L.lg + i;
+                    const float wr = s_w[buf * BM + r];
+                    float h[QN];
+                    float amax = 0.f;
 #pragma unroll
-                for (int q = 0; q < QN; ++q) {
-                    float g = acc[mt][2 * q][i], u = acc[mt][2 * q + 1][i];
-                    h[q] = swiglu_w(g, u, wr);
-                    amax = fmaxf(amax, __builtin_fabsf(h[q]));
-                }
-                // a 32-column group spans 32 / QN neighbouring lanes of the 16
-#pragma unroll
-                for (int o = 1; o < 32 / QN; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-                const int ex = e4m3_block_exp(amax);
-                const float inv = exp2_neg(ex);
-                const int col = icol0 + l16 * QN;
-                if (r < valid && col < p.I) {
-                    const int64_t pos = p0 + r;
-                    uint8_t* dst = p.hq + pos * p.I + col;
-                    static_assert(QN % 4 == 0, "whole dwords of E4M3 codes per lane");
-#pragma unroll
-                    for (int q = 0; q < QN; q += 4) {
-                        const uint32_t v = e4m3_pack4(h[q] * inv, h[q + 1] * inv, h[q + 2] * inv,
-                                                      h[q + 3] * inv);
-                        uint32_t* d = reinterpret_cast<uint32_t*>(dst + q);
-                        if constexpr (kCoh)
-                            __hip_atomic_store(d, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        else
-                            *d = v;
+                    for (int q = 0; q < QN; ++q) {
+                        const float g = acc[mt][2 * q][i], u = acc[mt][2 * q + 1][i];
+                        h[q] = swiglu_w(g, u, wr);
+                        amax = fmaxf(amax, __builtin_fabsf(h[q]));
                     }
-                    if ((col & (kGroup - 1)) == 0) {
-                        uint8_t* d = p.hsf + (int64_t)(col / (4 * kGroup)) * (p.T * p.topk) * 4 +
-                                     pos * 4 + (col / kGroup) % 4;
-                        if constexpr (kCoh)
-                            __hip_atomic_store(d, (uint8_t)(ex + 127), __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-                        else
-                            *d = (uint8_t)(ex + 127);
+                    // a 32-column group spans 32 / QN neighbouring lanes of the 16
+#pragma unroll
+                    for (int o = 1; o < 32 / QN; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+                    const int ex = e4m3_block_exp(amax);
+                    const float inv = exp2_neg(ex);
+                    const int col = icol0 + L.l16 * QN;
+                    if (r < valid && col < p.I) {
+                        const int64_t pos = p0 + r;
+                        uint8_t* dst = p.hq + pos * p.I + col;
+                        static_assert(QN % 4 == 0, "whole dwords of E4M3 codes per lane");
+#pragma unroll
+                        for (int q = 0; q < QN; q += 4) {
+                            const uint32_t v = e4m3_pack4(h[q] * inv, h[q + 1] * inv, h[q + 2] * inv,
+                                                          h[q + 3] * inv);
+                            uint32_t* d = reinterpret_cast<uint32_t*>(dst + q);
+                            if constexpr (kCoh)
+                                __hip_atomic_store(d, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            else
+                                *d = v;
+                        }
+                        if ((col & (kGroup - 1)) == 0) {
+                            uint8_t* d = p.hsf + (int64_t)(col / (4 * kGroup)) * (p.T * p.topk) * 4 +
+                                         pos * 4 + (col / kGroup) % 4;
+                            if constexpr (kCoh)
+                                __hip_atomic_store(d, (uint8_t)(ex + 127), __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                            else
+                                *d = (uint8_t)(ex + 127);
+                        }
                     }
                 }
             }
-        }
-    } else {
-        // lane holds row 4*lg + i, output columns n0 + l16*NT + nt, nt < NT
-        const int n0 = ntile * BN + wn * C::WTN + l16 * C::NT;
+        } else {
+            // lane holds row 4*lg + i, output columns n0 + l16*NT + nt, nt < NT
+            const int n0 = ntile * BN + L.wn * C::WTN + L.l16 * C::NT;
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) {
-            // one m-tile at a time: keeps the accumulators in AGPRs until used
-            __builtin_amdgcn_sched_barrier(0);
+            for (int mt = 0; mt < C::MT; ++mt) {
+                // one m-tile at a time: keeps the accumulators in AGPRs until used
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wm * C::WTM + mt * 16 + 4 * lg + i;
-                if (r < valid && n0 < p.H) {
-                    uint16_t* dst = p.o + (int64_t)(p0 + r) * p.H + n0;
-                    if constexpr (C::NT == 8) {
-                        uint4 v;
-                        v.x = f32_to_bf16(acc[mt][0][i]) | (f32_to_bf16(acc[mt][1][i]) << 16);
-                        v.y = f32_to_bf16(acc[mt][2][i]) | (f32_to_bf16(acc[mt][3][i]) << 16);
-                        v.z = f32_to_bf16(acc[mt][4][i]) | (f32_to_bf16(acc[mt][5][i]) << 16);
-                        v.w = f32_to_bf16(acc[mt][6][i]) | (f32_to_bf16(acc[mt][7][i]) << 16);
-                        *reinterpret_cast<uint4*>(dst) = v;
-                    } else {
+                for (int i = 0; i < 4; ++i) {
+                    const int r = L.wm * C::WTM + mt * 16 + 4 * L.lg + i;
+                    if (r < valid && n0 < p.H) {
+                        uint16_t* dst = p.o + (int64_t)(p0 + r) * p.H + n0;
+                        if constexpr (C::NT == 8) {
+                            uint4 v;
+                            v.x = f32_to_bf16(acc[mt][0][i]) | (f32_to_bf16(acc[mt][1][i]) << 16);
+                            v.y = f32_to_bf16(acc[mt][2][i]) | (f32_to_bf16(acc[mt][3][i]) << 16);
+                            v.z = f32_to_bf16(acc[mt][4][i]) | (f32_to_bf16(acc[mt][5][i]) << 16);
+                            v.w = f32_to_bf16(acc[mt][6][i]) | (f32_to_bf16(acc[mt][7][i]) << 16);
+                            *reinterpret_cast<uint4*>(dst) = v;
+                        } else {
 #pragma unroll
-                        for (int nt = 0; nt < C::NT; ++nt)
-                            dst[nt] = (uint16_t)f32_to_bf16(acc[mt][nt][i]);
+                            for (int nt = 0; nt < C::NT; ++nt)
+                                dst[nt] = (uint16_t)f32_to_bf16(acc[mt][nt][i]);
+                        }
                     }
                 }
             }
         }
     }
+};
+
+// One tile, loaded, computed and stored on its own (the one-launch kernel).
+template <int BM, int BN, int WM, int WN, bool kG1, bool kCoh>
+MOE_DEV void gemm_tile(const GemmParams& p, int mt, int ntile, uint8_t* smem) {
+    TileEngine<BM, BN, WM, WN, kG1, kCoh> eng(p, smem);
+    const int4 rec = p.mtile_rec[mt];        // {expert, first position, rows}
+    eng.load_rows_now(rec, 0);
+    eng.set_tile(rec, ntile, 0);
+    eng.zero_acc();
+    eng.prologue(0);
+    int st = 0;                                 // stage of step ks
+    for (int ks = 0; ks < eng.nk; ++ks) {
+        const int st2 = eng.next_stage(eng.next_stage(st));
+        eng.step(eng.stage_ptr(st), ks == 0, [] {}, [&] {
+            if (ks + 2 >= eng.nk) return false;
+            eng.issue(st2);
+            return true;
+        });
+        st = eng.next_stage(st);
+    }
+    eng.finish();
+    eng.epilogue(rec, ntile, 0);
     __syncthreads();
 }
 
@@ -488,18 +617,70 @@ MOE_DEV void grouped_order(int t, int m0, int nm, int nt, int* mt, int* ntile) {
     *mt = m0 + grp * kGM + (in_grp - *ntile * gm);
 }
 
-// GEMM1 or GEMM2 alone (one launch each, ordered by the stream).
+// GEMM1 or GEMM2 alone (one launch each, ordered by the stream).  The K
+// pipeline of a workgroup runs on across its tiles: while a tile is in its K
+// loop the next tile's rows are fetched (GEMM1, steps 1 and 2) and its load
+// sources set up (step nk - 2), and the last two steps issue the next tile's
+// first two K steps instead of reloading the current tile's last one, so the
+// epilogue overlaps those loads and the next tile starts on a full pipeline.
 template <int BM, int BN, int WM, int WN, bool kG1>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    __shared__ int s_tile[4];
+    using Eng = TileEngine<BM, BN, WM, WN, kG1, false>;
     const int NT = gemm_ntiles<BN>(p, kG1);
     const int mtiles = p.mtile_off[p.E];
     const int total = mtiles * NT;
-    for (int tile = xcd_slot(); tile < total; tile += gridDim.x) {
-        int mt, ntile;
-        grouped_order(tile, 0, mtiles, NT, &mt, &ntile);
-        gemm_tile<BM, BN, WM, WN, kG1, false>(p, mt, ntile, smem, s_tile);
+    int tile = xcd_slot();
+    if (tile >= total) return;
+    Eng eng(p, smem);
+    const int nk = eng.nk;
+    // rows fetched in steps 1 and 2 are published by the barrier ending step 2
+    const bool chain = nk >= (kG1 ? 5 : 2);
+    int mt, ntile;
+    grouped_order(tile, 0, mtiles, NT, &mt, &ntile);
+    int4 rec = p.mtile_rec[mt];                  // {expert, first position, rows}
+    int buf = 0, st = 0;                         // row buffer; LDS stage of the next step
+    eng.load_rows_now(rec, buf);
+    eng.set_tile(rec, ntile, buf);
+    eng.prologue(st);
+    for (;;) {
+        const int nxt = tile + gridDim.x;
+        const bool has_next = nxt < total;
+        int mt_n = mt, nt_n = ntile;
+        if (has_next) grouped_order(nxt, 0, mtiles, NT, &mt_n, &nt_n);
+        const int4 rec_n = p.mtile_rec[mt_n];
+        const bool pf = has_next && chain;
+        eng.zero_acc();
+        for (int ks = 0; ks < nk; ++ks) {
+            const int st2 = Eng::next_stage(Eng::next_stage(st));
+            eng.step(
+                eng.stage_ptr(st), ks == 0,
+                [&] {
+                    if (pf) {
+                        if (ks == 1 || ks == 2) eng.fetch_rows(rec_n, buf ^ 1, ks - 1);
+                        if (ks == nk - 2) eng.set_tile(rec_n, nt_n, buf ^ 1);
+                    }
+                },
+                [&] {
+                    if (ks + 2 >= nk && !pf) return false;
+                    eng.issue(st2);
+                    return true;
+                });
+            st = Eng::next_stage(st);
+        }
+        eng.finish();
+        eng.epilogue(rec, ntile, buf);
+        if (!has_next) break;
+        tile = nxt;
+        mt = mt_n;
+        ntile = nt_n;
+        rec = rec_n;
+        buf ^= 1;
+        if (!pf) {        // K too short to hide the next tile's set-up: do it here
+            eng.load_rows_now(rec, buf);
+            eng.set_tile(rec, ntile, buf);
+            eng.prologue(st);
+        }
     }
 }
 
@@ -518,7 +699,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    __shared__ int s_tile[4];
     const int tid = threadIdx.x;
     const int NT1 = gemm_ntiles<BN>(p, true), NT2 = gemm_ntiles<BN>(p, false);
     const int ew = p.wave_experts;
@@ -547,7 +727,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams 
         int mt, ntile;
         grouped_order(tile - seg_start, m0, nm, g1 ? NT1 : NT2, &mt, &ntile);
         if (g1) {
-            gemm_tile<BM, BN, WM, WN, true, true>(p, mt, ntile, smem, s_tile);
+            gemm_tile<BM, BN, WM, WN, true, true>(p, mt, ntile, smem);
             // every thread's coherent h stores have completed (vmcnt(0)) before the barrier
             __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8) | (0 << 14));
             __syncthreads();
@@ -566,7 +746,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams 
                 }
             }
             __syncthreads();
-            gemm_tile<BM, BN, WM, WN, false, true>(p, mt, ntile, smem, s_tile);
+            gemm_tile<BM, BN, WM, WN, false, true>(p, mt, ntile, smem);
         }
     }
 }
@@ -593,7 +773,7 @@ template <bool kG1>
 static hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     using C = Cfg<kBM, kBN, kWM, kWN, kG1>;
     auto kern = grouped_gemm_kernel<kBM, kBN, kWM, kWN, kG1>;
-    const size_t lds = C::kStages * (size_t)C::kStage + (size_t)kBM * 8;
+    const size_t lds = (size_t)C::kLds;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -616,7 +796,7 @@ hipError_t launch_gemm2(const GemmParams& p, hipStream_t s) { return launch_gemm
 hipError_t launch_fused_gemm(const GemmParams& p_in, hipStream_t s) {
     using C = Cfg<kBM, kBN, kWM, kWN, true>;
     auto kern = fused_gemm_kernel<kBM, kBN, kWM, kWN>;
-    const size_t lds = C::kStages * (size_t)C::kStage + (size_t)kBM * 8;
+    const size_t lds = (size_t)C::kLds;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute((const void*)kern,

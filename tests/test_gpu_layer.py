@@ -174,7 +174,7 @@ def test_forward_full_size_sampled_tokens(name):
     idx, _ = M.route(logits, w.topk, w.score_fn, bool(w.renorm))
     assert np.array_equal(inter["topk_idx"], idx)
     G.check_bucketize(inter, idx, w.E)
-    toks = [0, w.T - 1]
+    toks = [0, w.T // 3, 2 * w.T // 3, w.T - 1]
     ref = M.forward(dl.x_np, *G.oracle_weights(w), topk=w.topk, I=w.I, logits=logits,
                     tokens=toks)
     G.check_y(G.y_bits(y), ref["y"], rows=toks)
@@ -255,6 +255,31 @@ def test_narrow_and_tiled_gemms_match_oracle(w):
         ok = so_r >= 0
         G.check_hq(inter["hq"][so_g[ok]], inter["hsf"][so_g[ok]], ref["hq"][so_r[ok]],
                    ref["hsf"][so_r[ok]])
+        G.check_y(G.y_bits(y), ref["y"])
+
+
+# More tiles than workgroups, so that workgroups run several tiles back to back:
+# "chain" has enough K steps in both GEMMs for the next tile to be set up inside
+# the current one's K loop; "short_k" has too few (GEMM1 4 steps, GEMM2 1) and
+# sets up every tile after the previous one.
+MULTI_TILE_SHAPES = [W.Workload("chain", T=3072, H=768, I=512, E=8, topk=8),
+                     W.Workload("short_k", T=4096, H=512, I=128, E=8, topk=8)]
+
+
+@pytest.mark.parametrize("w", MULTI_TILE_SHAPES, ids=lambda w: w.name)
+def test_tiled_gemms_many_tiles_per_workgroup(w):
+    m = G.lib()
+    _log(f"many tiles per workgroup {w.name}")
+    dl = G.DeviceLayer(w)
+    ref = _oracle_full(w)
+    so_r = ref["slot_of"].reshape(-1)
+    for name, flag in (("tiled, two launches", m.FLAG_TILED),
+                       ("tiled, one launch", m.FLAG_ONE_LAUNCH)):
+        _log(f"  {name}")
+        y = dl.forward(flags=flag)
+        inter = dl.intermediates()
+        so_g = inter["slot_of"].reshape(-1)
+        G.check_hq(inter["hq"][so_g], inter["hsf"][so_g], ref["hq"][so_r], ref["hsf"][so_r])
         G.check_y(G.y_bits(y), ref["y"])
 
 
