@@ -46,17 +46,26 @@ MOE_DEV uint32_t float_order(float v) {
 // >= the candidate, each count a ballot and a popcount per value slot (no LDS
 // traffic).  The k keys >= T are then compacted into LDS and each is ranked
 // by the number of selected keys above it, which orders the slots.
+// One token's logits into the lanes (lane l: experts l, l + 64, ...).
 template <int NPL>
-MOE_DEV void route_token(const float* __restrict__ lrow, int E, int k, int score_fn, int renorm,
-                         int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-                         float* sel_v, int* sel_i, uint64_t* sel_k, int* lds_idx) {
+MOE_DEV void load_logits(const float* __restrict__ lrow, int E, float (&v)[NPL]) {
     const int lane = threadIdx.x & 63;
-    float v[NPL];
-    uint64_t key[NPL];
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int e = lane + 64 * i;
         v[i] = e < E ? lrow[e] : 0.0f;
+    }
+}
+
+template <int NPL>
+MOE_DEV void route_token(const float (&v)[NPL], int E, int k, int score_fn, int renorm,
+                         int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                         float* sel_v, int* sel_i, uint64_t* sel_k, int* lds_idx) {
+    const int lane = threadIdx.x & 63;
+    uint64_t key[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = lane + 64 * i;
         key[i] = e < E ? ((uint64_t)float_order(v[i]) << 10) | (uint64_t)(1023 - e) : 0;
     }
     uint64_t T = 0;
@@ -169,6 +178,23 @@ MOE_DEV void quant_rows(const RouteParams& p, int block, int nblocks) {
     }
 }
 
+// The tokens [t0, t0 + ntok) of this wave (i = wave, wave + kRouteWaves, ...),
+// the next token's logits loading while the current one is routed.
+template <int NPL>
+MOE_DEV void route_tokens(const RouteParams& p, int64_t t0, int ntok, int* pair_exp, float* sel_v,
+                          int* sel_i, uint64_t* sel_k) {
+    const int k = p.topk;
+    int i = threadIdx.x >> 6;
+    if (i >= ntok) return;
+    float v[NPL];
+    for (; i < ntok; i += kRouteWaves) {
+        const int64_t t = t0 + i;
+        load_logits<NPL>(p.logits + t * p.E, p.E, v);
+        route_token<NPL>(v, p.E, k, p.score_fn, p.renorm, p.idx_out + t * k, p.w_out + t * k, sel_v,
+                         sel_i, sel_k, pair_exp + i * k);
+    }
+}
+
 // Route tokens [t0, t0 + ntok) (one wave per token) or take the caller's ids;
 // pair i = (t - t0) * k + j of the chunk gets its expert in pair_exp[i].
 MOE_DEV void route_chunk(const RouteParams& p, int64_t t0, int ntok, int npl, int* pair_exp,
@@ -178,17 +204,11 @@ MOE_DEV void route_chunk(const RouteParams& p, int64_t t0, int ntok, int npl, in
     const int wave = tid >> 6;
     const int k = p.topk;
     if (p.logits) {
-        for (int i = wave; i < ntok; i += kRouteWaves) {
-            int64_t t = t0 + i;
-            const float* lr = p.logits + t * p.E;
-            int32_t* io = p.idx_out + t * k;
-            float* wo = p.w_out + t * k;
-            if (npl <= 1) route_token<1>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], sel_k[wave], pair_exp + i * k);
-            else if (npl <= 2) route_token<2>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], sel_k[wave], pair_exp + i * k);
-            else if (npl <= 4) route_token<4>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], sel_k[wave], pair_exp + i * k);
-            else if (npl <= 8) route_token<8>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], sel_k[wave], pair_exp + i * k);
-            else route_token<16>(lr, p.E, k, p.score_fn, p.renorm, io, wo, sel_v[wave], sel_i[wave], sel_k[wave], pair_exp + i * k);
-        }
+        if (npl <= 1) route_tokens<1>(p, t0, ntok, pair_exp, sel_v[wave], sel_i[wave], sel_k[wave]);
+        else if (npl <= 2) route_tokens<2>(p, t0, ntok, pair_exp, sel_v[wave], sel_i[wave], sel_k[wave]);
+        else if (npl <= 4) route_tokens<4>(p, t0, ntok, pair_exp, sel_v[wave], sel_i[wave], sel_k[wave]);
+        else if (npl <= 8) route_tokens<8>(p, t0, ntok, pair_exp, sel_v[wave], sel_i[wave], sel_k[wave]);
+        else route_tokens<16>(p, t0, ntok, pair_exp, sel_v[wave], sel_i[wave], sel_k[wave]);
     } else {
         for (int i = tid; i < ntok * k; i += kRouteThreads) {
             int e = p.idx_in[t0 * k + i];
@@ -239,11 +259,16 @@ MOE_DEV void route_count_block(const RouteParams& p, int npl) {
     }
 }
 
-// Blocks [0, ceil(T / kRouteTokensPerBlock)) route and count one chunk of
-// tokens each; every block then quantises its grid-stride share of x.
-__global__ __launch_bounds__(kRouteThreads) void route_count_quant_kernel(RouteParams p, int npl) {
-    if ((int64_t)blockIdx.x * kRouteTokensPerBlock < p.T) route_count_block(p, npl);
-    if (p.x) quant_rows(p, blockIdx.x, gridDim.x);
+// Blocks [0, route_blocks) route and count one chunk of kRouteTokensPerBlock
+// tokens each; the blocks after them quantise their grid-stride share of x
+// (the routing blocks, whose work is latency-bound, take no share).
+__global__ __launch_bounds__(kRouteThreads) void route_count_quant_kernel(RouteParams p, int npl,
+                                                                          int route_blocks) {
+    if ((int)blockIdx.x < route_blocks) {
+        route_count_block(p, npl);
+        return;
+    }
+    if (p.x) quant_rows(p, (int)blockIdx.x - route_blocks, (int)gridDim.x - route_blocks);
 }
 
 using BlockScan = rocprim::block_scan<int, kRouteThreads>;
@@ -270,18 +295,22 @@ MOE_DEV void block_exclusive_scan(const int* in, int* out, int n, BlockScan::sto
 }
 
 // Per-expert tables of the GEMMs from the final counts cnt[E] and their
-// exclusive scan off[E + 1] (one workgroup): counts, offsets, then m-tiles of
-// p.bm rows (tiled GEMMs) and sub-tiles of kSubRows rows (narrow GEMMs): per
-// expert ceil(count / rows) tiles, prefix-summed, one record per tile
-// {expert, first position, rows}, zero records up to the table's size.
+// exclusive scan off[E + 1]: counts, offsets, then m-tiles of p.bm rows (tiled
+// GEMMs) and sub-tiles of kSubRows rows (narrow GEMMs): per expert
+// ceil(count / rows) tiles, prefix-summed, one record per tile {expert, first
+// position, rows}, zero records up to the table's size.  Workgroup `part` of
+// `nparts` (each holding cnt and off) writes every nparts-th stretch of
+// records; part 0 also writes the per-expert arrays.
 MOE_DEV void write_tables(const ScatterParams& p, const int* cnt, const int* off, int* tiles,
-                          int* toff, BlockScan::storage_type& tmp) {
+                          int* toff, BlockScan::storage_type& tmp, int part, int nparts) {
     const int tid = threadIdx.x;
-    for (int e = tid; e < p.E; e += kRouteThreads) p.counts_out[e] = cnt[e];
-    for (int e = tid; e <= p.E; e += kRouteThreads) p.offsets_out[e] = off[e];
-    // the one-launch GEMMs' per-m-tile counters and status start at zero
-    for (int m = tid; m < p.max_mtiles; m += kRouteThreads) p.ready[m] = 0;
-    if (tid == 0) *p.status = 0;
+    if (part == 0) {
+        for (int e = tid; e < p.E; e += kRouteThreads) p.counts_out[e] = cnt[e];
+        for (int e = tid; e <= p.E; e += kRouteThreads) p.offsets_out[e] = off[e];
+        // the one-launch GEMMs' per-m-tile counters and status start at zero
+        for (int m = tid; m < p.max_mtiles; m += kRouteThreads) p.ready[m] = 0;
+        if (tid == 0) *p.status = 0;
+    }
     for (int pass = 0; pass < 2; ++pass) {
         const int rows = pass == 0 ? p.bm : kSubRows;
         const int cap = pass == 0 ? p.max_mtiles : p.max_subs;
@@ -290,7 +319,7 @@ MOE_DEV void write_tables(const ScatterParams& p, const int* cnt, const int* off
         __syncthreads();
         block_exclusive_scan(tiles, toff, p.E, tmp);
         const int ntiles = toff[p.E];
-        for (int m = tid; m < cap; m += kRouteThreads) {
+        for (int m = part * kRouteThreads + tid; m < cap; m += nparts * kRouteThreads) {
             int4 r = make_int4(0, 0, 0, 0);
             if (m < ntiles) {
                 int lo = 0, hi = p.E - 1;          // expert e with toff[e] <= m < toff[e+1]
@@ -304,10 +333,12 @@ MOE_DEV void write_tables(const ScatterParams& p, const int* cnt, const int* off
             }
             rec[m] = r;
         }
-        if (pass == 0) {
-            for (int e = tid; e <= p.E; e += kRouteThreads) p.mtile_off[e] = toff[e];
-        } else if (tid == 0) {
-            *p.nsub = ntiles;
+        if (part == 0) {
+            if (pass == 0) {
+                for (int e = tid; e <= p.E; e += kRouteThreads) p.mtile_off[e] = toff[e];
+            } else if (tid == 0) {
+                *p.nsub = ntiles;
+            }
         }
         __syncthreads();                          // tiles and toff are reused
     }
@@ -324,9 +355,10 @@ __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p)
     for (int e = tid; e < p.E; e += kRouteThreads)
         cnt[e] = __hip_atomic_load(&p.cnt[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    // every counter has been read by this block: report it, the last block resets them
+    // Every counter has been read by this block (the values are in LDS, past
+    // the barrier): report it; the last block to report resets them.  No fence:
+    // only the block's reads must precede its report, and they have returned.
     if (tid == 0) {
-        __threadfence();
         unsigned prev = atomicAdd(p.arrive, 1u);
         last = prev == gridDim.x - 1;
     }
@@ -335,7 +367,7 @@ __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p)
         for (int e = tid; e < p.E; e += kRouteThreads) p.cnt[e] = 0;
         if (tid == 0) *p.arrive = 0;
     }
-    if (blockIdx.x == 0) write_tables(p, cnt, off, tiles, toff, tmp);
+    write_tables(p, cnt, off, tiles, toff, tmp, blockIdx.x, gridDim.x);
     const int64_t npairs = p.T * p.topk;
     for (int64_t i = (int64_t)blockIdx.x * kRouteThreads + tid; i < npairs;
          i += (int64_t)gridDim.x * kRouteThreads) {
@@ -393,7 +425,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(RouteParams 
                 sp.slot_of[i] = -1;
             }
         }
-        write_tables(sp, hist, off, tiles, toff, tmp);
+        write_tables(sp, hist, off, tiles, toff, tmp, 0, 1);
         if (gridDim.x > 1) return;                    // the other workgroups quantise x
     }
     if (rp.x) {
@@ -412,17 +444,21 @@ hipError_t launch_route(const RouteParams& rp, const ScatterParams& sp, hipStrea
         return hipGetLastError();
     }
     if (rp.T > 0) {
-        int64_t route_blocks = (rp.T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
-        int64_t quant_blocks = rp.x ? (rp.T * (rp.H / 8) + 4 * kRouteThreads - 1) / (4 * kRouteThreads) : 0;
-        dim3 grid((unsigned)std::min<int64_t>(std::max(route_blocks, std::min<int64_t>(quant_blocks, 2048)),
-                                              1 << 30));
+        const int64_t route_blocks = (rp.T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
+        const int64_t quant_blocks =
+            rp.x ? (rp.T * (rp.H / 8) + 4 * kRouteThreads - 1) / (4 * kRouteThreads) : 0;
+        if (route_blocks + 2048 > (((int64_t)1 << 31) - 1)) return hipErrorInvalidValue;
+        dim3 grid((unsigned)(route_blocks + std::min<int64_t>(quant_blocks, 2048)));
         const int npl = rp.logits ? (rp.E + 63) / 64 : 1;
-        hipLaunchKernelGGL(route_count_quant_kernel, grid, dim3(kRouteThreads), 0, s, rp, npl);
+        hipLaunchKernelGGL(route_count_quant_kernel, grid, dim3(kRouteThreads), 0, s, rp, npl,
+                           (int)route_blocks);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
+    // one pair per thread (the scatter is a chain of dependent loads and stores)
     int64_t npairs = sp.T * sp.topk;
-    unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(1024, (npairs + 1023) / 1024));
+    unsigned blocks = (unsigned)std::max<int64_t>(
+        1, std::min<int64_t>(2048, (npairs + kRouteThreads - 1) / kRouteThreads));
     hipLaunchKernelGGL(scatter_kernel, dim3(blocks), dim3(kRouteThreads), 0, s, sp);
     return hipGetLastError();
 }
