@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--cpu-sample-experts", type=int, default=24,
                     help="experts whose rows the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--gemm-path", choices=("auto", "narrow", "tiled", "one-launch"),
+    ap.add_argument("--gemm-path", choices=("auto", "narrow", "tiled", "one-launch", "one-kernel"),
                     default="auto", help="GEMM kernels moe_forward uses (default: its own choice)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before the timed steps, copy a buffer of this many MiB once (a "
@@ -152,7 +152,25 @@ def gemm1_kernel_name(w, path) -> str:
     return "grouped_gemm_kernel<GEMM1> (tiled FP8xFP4 MFMA + SwiGLU*w -> FP8)"
 
 
-def roofline(w, counts, gemm1_ms, path="auto"):
+def layer_algorithmic_bytes(w, counts) -> float:
+    """Bytes the whole layer must move at least: W1|W3 and W2 codes and scales of every
+    expert that receives a row, x, the logits and y."""
+    touched = int((counts > 0).sum())
+    w13 = 2 * w.I * (w.H // 2 + w.H // 32)
+    w2 = w.H * (w.I // 2 + w.I // 32)
+    return touched * (w13 + w2) + w.T * (2 * w.H + 4 * w.E + 2 * w.H)
+
+
+def roofline(w, counts, stage_ms, path="auto"):
+    gemm1_ms = float(stage_ms[1])
+    if path == "one-kernel":
+        # the whole layer in one kernel: its minimum bytes over its duration
+        ms = float(sum(stage_ms))
+        alg_bytes = layer_algorithmic_bytes(w, counts)
+        gbs = alg_bytes / (ms * 1e-3) / 1e9
+        return {"kernel": "layer_small_kernel (route + quantise + narrow GEMMs + combine, one launch)",
+                "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "alg_bytes": alg_bytes}
     if path == "one-launch":
         # GEMM1 and GEMM2 in one kernel: all the layer's GEMM FLOPs over its duration
         tflops = w.flops() / (gemm1_ms * 1e-3) / 1e12
@@ -248,7 +266,7 @@ def main():
     nstage = m.NUM_STAGE_EVENTS
     ev = [(ctypes.c_void_p * nstage)(*[hip.event() for _ in range(nstage)]) for _ in range(a.steps)]
     flags = {"auto": m.FLAG_NONE, "narrow": m.FLAG_NARROW, "tiled": m.FLAG_TILED,
-             "one-launch": m.FLAG_ONE_LAUNCH}[a.gemm_path]
+             "one-launch": m.FLAG_ONE_LAUNCH, "one-kernel": m.FLAG_ONE_KERNEL}[a.gemm_path]
     args_plain = m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, flags=flags)
     args_ev = [m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, flags=flags,
                               stage_events=e) for e in ev]
@@ -304,7 +322,7 @@ def main():
         "layer_tflops": round(layer_tflops, 2),
         "layer_frac_mfma": round(layer_tflops / PEAK_MFMA_FP8_TFLOPS, 4),
         "stages_ms": {n: round(float(v), 4) for n, v in zip(m.STAGES, stage_ms)},
-        "roofline": roofline(w, counts, float(stage_ms[1]), a.gemm_path),
+        "roofline": roofline(w, counts, stage_ms, a.gemm_path),
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_experts)

@@ -82,12 +82,20 @@ typedef struct moe_dims {
  * tiles wait on per-m-tile ready counters, experts grouped in waves ("MegaMoE"
  * notes, "Scheduler" and "Wave"); on one MI355X it measured slower than the
  * two launches at the DeepSeek-V3-like and 256-expert shapes, so it is not
- * the default.  All paths meet the same tolerance against the definition.
- * NARROW together with TILED or ONE_LAUNCH is MOE_EINVAL. */
+ * the default.  MOE_FLAG_ONE_KERNEL runs the whole layer (routing, bucketing,
+ * quantisation, the narrow GEMMs and the combine) as one cooperative launch
+ * whose phases are separated by grid barriers ("MonoMoe kernel — design" §1);
+ * it needs T * topk <= 1024 (else MOE_EUNSUPPORTED) and implies the narrow
+ * GEMMs.  On one MI355X its grid barriers (cache write-backs between XCDs)
+ * cost more than the launch boundaries they replace, so it is not the
+ * default either.  All paths meet the same tolerance against the definition.  NARROW
+ * together with TILED or ONE_LAUNCH is MOE_EINVAL, and so is ONE_KERNEL
+ * together with TILED or ONE_LAUNCH. */
 #define MOE_FLAG_NONE 0u
 #define MOE_FLAG_NARROW 1u
 #define MOE_FLAG_TILED 2u
 #define MOE_FLAG_ONE_LAUNCH 4u
+#define MOE_FLAG_ONE_KERNEL 8u
 
 #define MOE_NUM_STAGE_EVENTS 5
 
@@ -110,7 +118,8 @@ typedef struct moe_dims {
  *             are recorded on s before routing, before GEMM1, before GEMM2,
  *             before the combine and after it (for per-stage timing); with
  *             MOE_FLAG_ONE_LAUNCH the third is recorded after that launch,
- *             right before the fourth. */
+ *             right before the fourth; with MOE_FLAG_ONE_KERNEL the second,
+ *             third and fourth are recorded after the one launch. */
 typedef struct moe_args {
     moe_dims_t dims;
     const uint16_t* x;

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "quant.hip", "gemm.hip", "narrow.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "quant.hip", "gemm.hip", "narrow.hip", "combine.hip", "layer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

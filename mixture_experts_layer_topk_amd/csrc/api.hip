@@ -222,11 +222,12 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     if (d.T == 0) return MOE_OK;
     if (!a->x || !a->w13 || !a->w13_sf || !a->w2 || !a->w2_sf || !a->y || !a->ws) return MOE_EINVAL;
     if (!a->logits && (!a->topk_idx || !a->topk_w)) return MOE_EINVAL;
-    if ((a->flags & ~(MOE_FLAG_NARROW | MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH)) ||
-        (a->flags & (MOE_FLAG_NARROW | MOE_FLAG_TILED)) == (MOE_FLAG_NARROW | MOE_FLAG_TILED) ||
-        (a->flags & (MOE_FLAG_NARROW | MOE_FLAG_ONE_LAUNCH)) ==
-            (MOE_FLAG_NARROW | MOE_FLAG_ONE_LAUNCH))
+    const uint32_t f = a->flags;
+    if ((f & ~(MOE_FLAG_NARROW | MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH | MOE_FLAG_ONE_KERNEL)) ||
+        ((f & MOE_FLAG_NARROW) && (f & (MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH))) ||
+        ((f & MOE_FLAG_ONE_KERNEL) && (f & (MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH))))
         return MOE_EINVAL;
+    if ((f & MOE_FLAG_ONE_KERNEL) && !moe::layer_small_fits(d.T, d.topk)) return MOE_EUNSUPPORTED;
     if (!aligned16(a->x) || !aligned16(a->w13) || !aligned16(a->w2) || !aligned16(a->y) ||
         ((uintptr_t)a->w13_sf & 3) || ((uintptr_t)a->w2_sf & 3))
         return MOE_EINVAL;
@@ -275,7 +276,8 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     sp.status = at<int>(ws, c.status);
     hipEvent_t* ev = a->stage_events;
     hipError_t err = ev ? hipEventRecord(ev[0], s) : hipSuccess;
-    if (err == hipSuccess) err = moe::launch_route(rp, sp, s);
+    const bool one_kernel = (f & MOE_FLAG_ONE_KERNEL) != 0;
+    if (err == hipSuccess && !one_kernel) err = moe::launch_route(rp, sp, s);
     if (err != hipSuccess) return hip_fail(err);
 
     moe::GemmParams gp{};
@@ -306,6 +308,17 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     const int64_t R = d.T * d.topk;
     gp.max_mtiles = (int)max_mtiles(d);
     gp.max_subs = (int)max_subs(d);
+    if (one_kernel) {
+        moe::LayerParams lp{};
+        lp.y = a->y;
+        lp.count = at<unsigned>(ws, c.arrive) + 4;
+        lp.exits = at<unsigned>(ws, c.arrive) + 8;
+        lp.status = sp.status;
+        err = moe::launch_layer_small(rp, sp, gp, lp, s);
+        for (int i = 1; i < MOE_NUM_STAGE_EVENTS && err == hipSuccess && ev; ++i)
+            err = hipEventRecord(ev[i], s);
+        return err == hipSuccess ? MOE_OK : hip_fail(err);
+    }
     // few rows per expert on average: the weight-streaming (narrow) kernels
     bool narrow = R <= kNarrowRowsPerExpert * (int64_t)d.E;
     if (a->flags & MOE_FLAG_NARROW) narrow = true;

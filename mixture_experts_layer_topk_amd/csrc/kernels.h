@@ -100,4 +100,18 @@ hipError_t launch_narrow_gemm2(const GemmParams& p, hipStream_t s);
 hipError_t launch_combine(const uint16_t* o, const int32_t* slot_of, int64_t T, int topk, int H,
                           uint16_t* y, hipStream_t s);
 
+// The whole layer in one cooperative launch for T * topk <= 1024 (routing and
+// bucketing in one workgroup, narrow GEMMs, combine), phases separated by
+// grid barriers on two counters that are zero between launches.
+struct LayerParams {
+    uint16_t* y;                // [T, H] layer output
+    unsigned* count;            // barrier arrivals (zero on entry, reset on exit)
+    unsigned* exits;            // workgroups that have left (zero on entry, reset on exit)
+    int* status;                // [1] set to 2 if a barrier wait gave up
+    int npl;                    // logits per lane of the routing waves (set by the launcher)
+};
+bool layer_small_fits(int64_t T, int topk);
+hipError_t launch_layer_small(const RouteParams& rp, const ScatterParams& sp, const GemmParams& gp,
+                              LayerParams lp, hipStream_t s);
+
 }  // namespace moe

@@ -1,0 +1,226 @@
+// Device code of the narrow (weight-streaming) grouped GEMMs, shared by their
+// launches and the one-kernel layer.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+#include "mfma.h"
+
+namespace moe {
+
+constexpr int kNarrowWaves = 4;
+constexpr int kNarrowThreads = 64 * kNarrowWaves;
+constexpr int kNT = 4;                  // 16-column MFMA tiles per unit
+constexpr int kBatch = kNarrowThreads / kSubRows;   // unit headers fetched per batch
+constexpr int kNarrowBlocksPerCU = 2;
+
+template <bool kG1>
+struct NarrowCfg {
+    static constexpr int kCols = kG1 ? 32 : 64;         // I columns (GEMM1) or H columns
+    static constexpr int KC = 1;                        // K steps per item and wave
+    static constexpr int NBUF = 4;                      // items in flight per wave
+};
+
+template <int KC>
+struct NarrowBuf {
+    v4i b[KC][kNT];
+    uint32_t sb[KC][kNT];
+    v4i alo[KC], ahi[KC];
+    uint32_t sa[KC];
+};
+
+// The GEMM of workgroup `bid` of `G` (any G >= 1: the units are dealt out
+// persistently).
+template <bool kG1>
+MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
+    using Cfg = NarrowCfg<kG1>;
+    constexpr int KC = Cfg::KC, NBUF = Cfg::NBUF;
+    __shared__ v4f s_red[kNarrowWaves][kNT][64];       // partial accumulators
+    __shared__ int s_hdr[kBatch][4];                   // expert, first position, rows, chunk
+    __shared__ int s_arow[kBatch][kSubRows];           // activation row of each unit row
+    __shared__ float s_w[kBatch][kSubRows];            // routing weight (GEMM1)
+    __shared__ float s_amax[2][16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int nch = (kG1 ? p.I : p.H) / Cfg::kCols;
+    const int nunits = *p.nsub * nch;
+
+    const int K = kG1 ? p.H : p.I;
+    const int nk = K / kKStep;
+    const int64_t R = p.T * p.topk;
+    const int64_t wrows = kG1 ? 2 * (int64_t)p.I : p.H;  // weight rows of one expert
+    const uint8_t* wq = kG1 ? p.w13 : p.w2;
+    const uint8_t* wsf = kG1 ? p.w13sf : p.w2sf;
+    const uint8_t* aq = kG1 ? p.xq : p.hq;
+    const uint8_t* asf = kG1 ? p.xsf : p.hsf;
+    const int64_t a_slab = 4 * (kG1 ? p.T : R);          // bytes per K step of activation scales
+    const int64_t w_slab = 4 * wrows;                    // bytes per K step of weight scales
+    // this wave's K range; every wave runs nchunk items per unit
+    const int kb = wave * nk / kNarrowWaves, ke = (wave + 1) * nk / kNarrowWaves;
+    const int kr = (nk + kNarrowWaves - 1) / kNarrowWaves;
+    const int nchunk = (kr + KC - 1) / KC;
+
+    // weight row (= output column) of this lane in tile t of column chunk nc
+    auto brow = [&](int nc, int t) -> int {
+        if (kG1) {
+            const int icol = nc * Cfg::kCols + (t & 1) * 16 + l16;
+            return (t >> 1) ? p.I + icol : icol;         // tiles 0, 1 gate; 2, 3 up
+        }
+        return nc * Cfg::kCols + 16 * t + l16;
+    };
+
+    for (int u0 = bid; u0 < nunits; u0 += kBatch * G) {
+        // ---- headers of units u0 + j * G, j < kBatch (16 threads per unit)
+        __syncthreads();                                // the previous batch is done with LDS
+        {
+            const int j = tid / kSubRows, r = tid % kSubRows;
+            const int u = u0 + j * G;
+            if (u < nunits) {
+                const int m = u / nch;
+                const int4 rec = p.sub_rec[m];          // {expert, first position, rows}
+                const int pos = rec.y + min(r, rec.z - 1);
+                int arow = pos;
+                float w = 0.0f;
+                if (kG1) {
+                    const int src = p.slot_src[pos];
+                    arow = src / p.topk;
+                    w = p.topk_w[src];
+                }
+                s_arow[j][r] = arow;
+                s_w[j][r] = w;
+                if (r == 0) {
+                    s_hdr[j][0] = rec.x;
+                    s_hdr[j][1] = rec.y;
+                    s_hdr[j][2] = rec.z;
+                    s_hdr[j][3] = u - m * nch;
+                }
+            }
+        }
+        __syncthreads();
+        const int nb = min(kBatch, (nunits - u0 + G - 1) / G);
+        const int nitems = nb * nchunk;
+
+        // ---- item q: unit q / nchunk, K steps kb + (q % nchunk) * KC + [0, KC)
+        // Items past the end re-read the last one (cached) and K steps past the
+        // wave's range re-read one inside it, so every path issues the same loads
+        // and the compiler's counted waits keep the later buffers in flight.
+        auto issue = [&](NarrowBuf<KC>& bf, int q) {
+            q = min(q, nitems - 1);
+            const int j = q / nchunk, c = q - j * nchunk;
+            const int e = s_hdr[j][0], nc = s_hdr[j][3];
+            const int64_t arow = s_arow[j][l16];
+            const uint8_t* wq_e = wq + (int64_t)e * wrows * (K / 2) + lg * 16;
+            const uint8_t* wsf_e = wsf + (int64_t)e * nk * w_slab;
+            const uint8_t* ap = aq + arow * K + lg * 16;
+            const uint8_t* asp = asf + arow * 4;
+#pragma unroll
+            for (int jj = 0; jj < KC; ++jj) {
+                const int ks = max(0, min(kb + c * KC + jj, min(ke, nk) - 1));
+#pragma unroll
+                for (int t = 0; t < kNT; ++t) {
+                    const int br = brow(nc, t);
+                    bf.b[jj][t] = *reinterpret_cast<const v4i*>(wq_e + (int64_t)br * (K / 2) +
+                                                                ks * (kKStep / 2));
+                    bf.sb[jj][t] = *reinterpret_cast<const uint32_t*>(wsf_e + ks * w_slab + br * 4);
+                }
+                bf.alo[jj] = *reinterpret_cast<const v4i*>(ap + ks * kKStep);
+                bf.ahi[jj] = *reinterpret_cast<const v4i*>(ap + ks * kKStep + 64);
+                bf.sa[jj] = *reinterpret_cast<const uint32_t*>(asp + ks * a_slab);
+            }
+        };
+
+        v4f acc[kNT];
+        auto epilogue = [&](int j) {
+            const int p0 = s_hdr[j][1], valid = s_hdr[j][2], nc = s_hdr[j][3];
+            __syncthreads();                            // s_red of the previous unit is read
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) s_red[wave][t][lane] = acc[t];
+            __syncthreads();
+            // lane holds rows 4 lg + i (i < 4), column l16 of a tile
+            if (kG1) {
+                // wave 0: I columns [c, c+16) (tiles 0, 2); wave 1: [c+16, c+32) (tiles 1, 3)
+                float h[4] = {0.f, 0.f, 0.f, 0.f};
+                if (wave < 2) {
+                    v4f g = s_red[0][wave][lane], u = s_red[0][2 + wave][lane];
+#pragma unroll
+                    for (int w = 1; w < kNarrowWaves; ++w) {
+                        g += s_red[w][wave][lane];
+                        u += s_red[w][2 + wave][lane];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        h[i] = swiglu_w(g[i], u[i], s_w[j][4 * lg + i]);
+                        float m = __builtin_fabsf(h[i]);
+#pragma unroll
+                        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+                        if (l16 == 0) s_amax[wave][4 * lg + i] = m;
+                    }
+                }
+                // an E4M3 group is the unit's 32 I columns: both waves' maxima
+                __syncthreads();
+                if (wave < 2) {
+                    const int icol = nc * Cfg::kCols + wave * 16 + l16;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 4 * lg + i;
+                        const int ex =
+                            e4m3_block_exp(fmaxf(s_amax[0][4 * lg + i], s_amax[1][4 * lg + i]));
+                        if (r < valid) {
+                            const int64_t pos = p0 + r;
+                            p.hq[pos * p.I + icol] = (uint8_t)e4m3_pack2(h[i] * exp2_neg(ex), 0.0f);
+                            if (wave == 0 && l16 == 0)
+                                p.hsf[(int64_t)(icol / (4 * kGroup)) * (R * 4) + pos * 4 +
+                                      (icol / kGroup) % 4] = (uint8_t)(ex + 127);
+                        }
+                    }
+                }
+            } else {
+                v4f o = s_red[0][wave][lane];
+#pragma unroll
+                for (int w = 1; w < kNarrowWaves; ++w) o += s_red[w][wave][lane];
+                const int col = brow(nc, wave);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * lg + i;
+                    if (r < valid) p.o[(int64_t)(p0 + r) * p.H + col] = (uint16_t)f32_to_bf16(o[i]);
+                }
+            }
+        };
+        auto consume = [&](const NarrowBuf<KC>& bf, int q) {
+            const int j = q / nchunk, c = q - j * nchunk;
+            if (c == 0) {
+#pragma unroll
+                for (int t = 0; t < kNT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int jj = 0; jj < KC; ++jj) {
+                if (kb + c * KC + jj < ke) {
+                    const v8i a = v8i{bf.alo[jj][0], bf.alo[jj][1], bf.alo[jj][2], bf.alo[jj][3],
+                                      bf.ahi[jj][0], bf.ahi[jj][1], bf.ahi[jj][2], bf.ahi[jj][3]};
+                    // lane group lg supplies the scale of K group lg of the step
+                    const int sa = (int)(bf.sa[jj] >> (8 * lg));
+#pragma unroll
+                    for (int t = 0; t < kNT; ++t)
+                        acc[t] = mfma_fp8_fp4(a, bf.b[jj][t], acc[t], sa, (int)(bf.sb[jj][t] >> (8 * lg)));
+                }
+            }
+            if (c == nchunk - 1) epilogue(j);
+        };
+
+        NarrowBuf<KC> buf[NBUF];
+#pragma unroll
+        for (int q = 0; q < NBUF - 1; ++q) issue(buf[q], q);
+        for (int q0 = 0; q0 < nitems; q0 += NBUF) {
+#pragma unroll
+            for (int b = 0; b < NBUF; ++b) {
+                issue(buf[(b + NBUF - 1) % NBUF], q0 + b + NBUF - 1);
+                if (q0 + b < nitems) consume(buf[b], q0 + b);
+            }
+        }
+    }
+}
+
+
+}  // namespace moe

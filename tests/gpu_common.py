@@ -111,7 +111,7 @@ class DeviceLayer:
                           logits=self.logits, flags=flags)
         torch.cuda.synchronize()
         status = int(m.intermediates(self.d, self.ws)["status"].item())
-        assert status == 0, "a GEMM2 tile gave up waiting for its GEMM1 tiles"
+        assert status == 0, f"a wait inside the layer gave up (status {status})"
         return y
 
     def intermediates(self):

@@ -246,8 +246,11 @@ def test_narrow_and_tiled_gemms_match_oracle(w):
     dl = G.DeviceLayer(w, external_topk=ext)
     ref = _oracle_full(w, ext)
     so_r = ref["slot_of"].reshape(-1)
-    for name, flag in (("narrow", m.FLAG_NARROW), ("tiled, two launches", m.FLAG_TILED),
-                       ("tiled, one launch", m.FLAG_ONE_LAUNCH)):
+    paths = [("narrow", m.FLAG_NARROW), ("tiled, two launches", m.FLAG_TILED),
+             ("tiled, one launch", m.FLAG_ONE_LAUNCH)]
+    if w.T * w.topk <= 1024:
+        paths.append(("whole layer, one kernel", m.FLAG_ONE_KERNEL))
+    for name, flag in paths:
         _log(f"  {name}")
         y = dl.forward(use_logits=ext is None, flags=flag)
         inter = dl.intermediates()
@@ -296,6 +299,29 @@ def test_one_launch_reads_this_calls_h():
     for dl, ref in ((da, ra), (db, rb), (da, ra), (db, rb)):
         y = dl.forward(flags=m.FLAG_ONE_LAUNCH)
         G.check_y(G.y_bits(y), ref["y"])
+
+
+def test_one_kernel_layer_reads_this_calls_data():
+    """The one-kernel layer on alternating inputs and shapes sharing one workspace: a
+    phase that read a previous call's activations, tables or GEMM outputs from a stale
+    cache line (instead of what this call's earlier phase stored), or a barrier counter
+    left non-zero by the previous call, would give the other input's result."""
+    m = G.lib()
+    wa = W.WORKLOADS["decode"]
+    wb = W.Workload("decode_b", T=8, H=2048, I=512, E=256, topk=8, seed=1)
+    wc = W.Workload("mid_b", T=96, H=2048, I=512, E=32, topk=8, seed=2)
+    _log("one kernel, alternating inputs")
+    da, db, dc = G.DeviceLayer(wa), G.DeviceLayer(wb), G.DeviceLayer(wc)
+    db.ws = da.ws
+    if dc.ws.numel() > da.ws.numel():
+        da.ws = db.ws = dc.ws
+    else:
+        dc.ws = da.ws
+    refs = [_oracle_full(w) for w in (wa, wb, wc)]
+    for _ in range(2):
+        for dl, ref in zip((da, db, dc), refs):
+            y = dl.forward(flags=m.FLAG_ONE_KERNEL)
+            G.check_y(G.y_bits(y), ref["y"])
 
 
 def test_scales_kmajor_is_a_transpose():

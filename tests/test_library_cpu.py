@@ -71,10 +71,17 @@ def test_forward_rejects_null_and_small_workspace_without_gpu():
     a.ws = ctypes.c_void_p(1 << 20)
     assert m._lib.moe_forward(ctypes.byref(a), None) == m.MOE_EINVAL
     a.x = fake
-    for bad_flags in (m.FLAG_NARROW | m.FLAG_TILED, m.FLAG_NARROW | m.FLAG_ONE_LAUNCH, 8,
-                      1 << 31):                                                # unknown or conflicting
+    for bad_flags in (m.FLAG_NARROW | m.FLAG_TILED, m.FLAG_NARROW | m.FLAG_ONE_LAUNCH,
+                      m.FLAG_ONE_KERNEL | m.FLAG_TILED, m.FLAG_ONE_KERNEL | m.FLAG_ONE_LAUNCH,
+                      16, 1 << 31):                                            # unknown or conflicting
         a.flags = bad_flags
         assert m._lib.moe_forward(ctypes.byref(a), None) == m.MOE_EINVAL
+    # the one-kernel layer takes at most 1024 routed pairs
+    big = m.dims(129, 256, 128, 32, 8)
+    a.dims = big
+    a.ws_bytes = m.workspace_size(big)
+    a.flags = m.FLAG_ONE_KERNEL
+    assert m._lib.moe_forward(ctypes.byref(a), None) == m.MOE_EUNSUPPORTED
 
 
 def test_quant_and_pack_reject_bad_sizes():
