@@ -199,6 +199,8 @@ struct TileEngine {
     const uint8_t* ld_sa;
     const uint8_t* ld_sw;
     bool late;                  // the second wave of this SIMD (wm == 1)
+    int wm_u;                   // wm of this wave (uniform)
+    bool rows;                  // this wave's 64 rows of the tile hold rows of the expert
     bool sa_wave;               // an early wave that loads an A-scale block
     int lg;
     int a_lo, a_hi, b_fr, sa_fr, sb_fr;
@@ -249,6 +251,8 @@ struct TileEngine {
         sa_base = kG1 ? p.xsf : p.hsf;
         const Lane L;
         late = __builtin_amdgcn_readfirstlane(L.wm) == 1;
+        wm_u = __builtin_amdgcn_readfirstlane(L.wm);
+        rows = true;
         sa_wave = !late && __builtin_amdgcn_readfirstlane(L.wave) < C::kSABlocks;
         lg = L.lg;
         // MFMA operands.  Fragment addresses of different tiles differ by
@@ -376,6 +380,13 @@ struct TileEngine {
         ld_sw += sb_slab;
     }
 
+    // Rows of the tile in the K loop: a wave whose WTM rows all lie past the
+    // expert's last row (the late wave in the last m-tile of an expert with
+    // at most WTM rows there) skips its MFMAs; its outputs are never stored.
+    // (Skipping single 16-row m-tiles instead made the compiler spill the
+    // accumulators.)
+    __device__ __forceinline__ void set_rows(int valid) { rows = valid > wm_u * C::WTM; }
+
     __device__ __forceinline__ void zero_acc() {
 #pragma unroll
         for (int i = 0; i < C::MT; ++i)
@@ -406,12 +417,14 @@ struct TileEngine {
         for (int mt = 0; mt < C::MT; ++mt) sa[mt] = (int)((uint32_t)sa_run[mt / 4][mt % 4] >> (8 * lg));
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) sb[nt] = (int)((uint32_t)sb_run[nt / 4][nt % 4] >> (8 * lg));
+        if (rows) {
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) {
-            __builtin_amdgcn_sched_barrier(0);
+            for (int nt = 0; nt < C::NT; ++nt) {
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int mt = 0; mt < C::MT; ++mt)
-                acc[mt][nt] = mfma_fp8_fp4(a[mt], b[nt], acc[mt][nt], sa[mt], sb[nt]);
+                for (int mt = 0; mt < C::MT; ++mt)
+                    acc[mt][nt] = mfma_fp8_fp4(a[mt], b[nt], acc[mt][nt], sa[mt], sb[nt]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -576,6 +589,7 @@ MOE_DEV void gemm_tile(const GemmParams& p, int mt, int ntile, uint8_t* smem) {
     const int4 rec = p.mtile_rec[mt];        // {expert, first position, rows}
     eng.load_rows_now(rec, 0);
     eng.set_tile(rec, ntile, 0);
+    eng.set_rows(rec.z);
     eng.zero_acc();
     eng.prologue(0);
     int st = 0;                                 // stage of step ks
@@ -650,6 +664,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
         if (has_next) grouped_order(nxt, 0, mtiles, NT, &mt_n, &nt_n);
         const int4 rec_n = p.mtile_rec[mt_n];
         const bool pf = has_next && chain;
+        eng.set_rows(rec.z);
         eng.zero_acc();
         for (int ks = 0; ks < nk; ++ks) {
             const int st2 = Eng::next_stage(Eng::next_stage(st));
