@@ -17,8 +17,12 @@ constexpr int kNarrowBlocksPerCU = 2;
 template <bool kG1>
 struct NarrowCfg {
     static constexpr int kCols = kG1 ? 32 : 64;         // I columns (GEMM1) or H columns
-    static constexpr int KC = 1;                        // K steps per item and wave
-    static constexpr int NBUF = 4;                      // items in flight per wave
+    // K steps per item and wave, items in flight per wave.  GEMM1 loads two
+    // K steps per item, so the two 64-byte halves of a weight row's 128-byte
+    // line are requested together (6% faster at the decode shape); GEMM2's
+    // K = I is too short per wave for that (each wave has I / 512 steps).
+    static constexpr int KC = kG1 ? 2 : 1;
+    static constexpr int NBUF = kG1 ? 2 : 4;
 };
 
 template <int KC>
