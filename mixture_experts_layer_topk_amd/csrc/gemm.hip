@@ -418,11 +418,13 @@ struct TileEngine {
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) sb[nt] = (int)((uint32_t)sb_run[nt / 4][nt % 4] >> (8 * lg));
         if (rows) {
+            // m-tile outer: consecutive MFMAs share their A fragment (measured
+            // 0.6% faster than sharing B)
 #pragma unroll
-            for (int nt = 0; nt < C::NT; ++nt) {
+            for (int mt = 0; mt < C::MT; ++mt) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int mt = 0; mt < C::MT; ++mt)
+                for (int nt = 0; nt < C::NT; ++nt)
                     acc[mt][nt] = mfma_fp8_fp4(a[mt], b[nt], acc[mt][nt], sa[mt], sb[nt]);
             }
         }

@@ -264,9 +264,12 @@ def test_narrow_and_tiled_gemms_match_oracle(w):
 # More tiles than workgroups, so that workgroups run several tiles back to back:
 # "chain" has enough K steps in both GEMMs for the next tile to be set up inside
 # the current one's K loop; "short_k" has too few (GEMM1 4 steps, GEMM2 1) and
-# sets up every tile after the previous one.
+# sets up every tile after the previous one; "chain_k2" chains GEMM2 tiles of
+# the fewest K steps that allow it (2), so the next tile's set-up shares the
+# step that issues its first loads.
 MULTI_TILE_SHAPES = [W.Workload("chain", T=3072, H=768, I=512, E=8, topk=8),
-                     W.Workload("short_k", T=4096, H=512, I=128, E=8, topk=8)]
+                     W.Workload("short_k", T=4096, H=512, I=128, E=8, topk=8),
+                     W.Workload("chain_k2", T=4096, H=512, I=256, E=8, topk=8)]
 
 
 @pytest.mark.parametrize("w", MULTI_TILE_SHAPES, ids=lambda w: w.name)
