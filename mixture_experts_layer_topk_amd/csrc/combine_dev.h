@@ -44,10 +44,10 @@ MOE_DEV void combine_chunk(const uint16_t* __restrict__ o, const int32_t* __rest
         acc[6] += bf16_to_f32(raw[j].w & 0xFFFFu); acc[7] += bf16_to_f32(raw[j].w >> 16);
     }
     uint4 out;
-    out.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-    out.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-    out.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-    out.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+    out.x = pack_bf16x2(acc[0], acc[1]);
+    out.y = pack_bf16x2(acc[2], acc[3]);
+    out.z = pack_bf16x2(acc[4], acc[5]);
+    out.w = pack_bf16x2(acc[6], acc[7]);
     store_once(reinterpret_cast<uint4*>(y + t * H + c), out);
 }
 

@@ -39,6 +39,14 @@ MOE_DEV uint32_t f32_to_bf16(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two floats to BF16, round to nearest even, packed lo | hi << 16 (one
+// v_cvt_pk_bf16_f32 on gfx950; the same result as f32_to_bf16 on finite values).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
+
 // Block exponent e (clamped to [-127, 127]) for a group whose largest
 // magnitude is amax (finite, >= 0).  kMantThresh is the mantissa field of
 // Q's significand: 0x600000 (1.75, E4M3) or 0x400000 (1.5, E2M1); kShift is

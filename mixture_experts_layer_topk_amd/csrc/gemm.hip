@@ -152,6 +152,19 @@ MOE_DEV void barrier_nofence() {
 // the 16 lanes of one lane group read 256 consecutive bytes (no conflicts).
 MOE_DEV int scale_slot_row(int q) { return (q & ~63) | ((q & 3) << 4) | ((q >> 2) & 15); }
 
+// Largest value over each group of 8 neighbouring lanes (lanes 8j .. 8j + 7),
+// with DPP row operations instead of LDS round trips: swap neighbours, swap
+// pairs (each quad then holds its maximum), then mirror the 8-lane half-row
+// (quad 0 meets quad 1).  Inputs are finite.
+MOE_DEV float max_of_8_lanes(float v) {
+    float m = __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v = v > m ? v : m;
+    m = __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xF, 0xF, false);         // quad_perm [2,3,0,1]
+    v = v > m ? v : m;
+    m = __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xF, 0xF, false);        // row_half_mirror
+    return v > m ? v : m;
+}
+
 // kAux: cache policy bits of the load (kCohAux: device-coherent, sc1)
 constexpr int kCohAux = 16;
 constexpr int kSpinLimit = 1 << 24;     // polls of a ready counter before giving up (~0.5 s)
@@ -504,15 +517,19 @@ struct TileEngine {
             // lane holds, for row 4*lg + i of m-tile mt, the h columns
             // icol0 + l16*(NT/2) + q, q < NT/2 (gate acc[2q], up acc[2q+1])
             constexpr int QN = C::NT / 2;
+            static_assert(QN == 4, "a 32-column E4M3 group is 8 neighbouring lanes");
             const int icol0 = ntile * (BN / 2) + L.wn * (C::WTN / 2);
 #pragma unroll
             for (int mt = 0; mt < C::MT; ++mt) {
-                // one m-tile at a time: keeps the accumulators in AGPRs until used
+                // one m-tile at a time: bounds the registers live in the epilogue
                 __builtin_amdgcn_sched_barrier(0);
+                // routing weights of this lane's rows 4 lg + i of the m-tile
+                const v4f wrow =
+                    *reinterpret_cast<const v4f*>(s_w + buf * BM + L.wm * C::WTM + mt * 16 + 4 * L.lg);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = L.wm * C::WTM + mt * 16 + 4 * L.lg + i;
-                    const float wr = s_w[buf * BM + r];
+                    const float wr = wrow[i];
                     float h[QN];
                     float amax = 0.f;
 #pragma unroll
@@ -521,9 +538,7 @@ struct TileEngine {
                         h[q] = swiglu_w(g, u, wr);
                         amax = fmaxf(amax, __builtin_fabsf(h[q]));
                     }
-                    // a 32-column group spans 32 / QN neighbouring lanes of the 16
-#pragma unroll
-                    for (int o = 1; o < 32 / QN; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+                    amax = max_of_8_lanes(amax);
                     const int ex = e4m3_block_exp(amax);
                     const float inv = exp2_neg(ex);
                     const int col = icol0 + L.l16 * QN;
@@ -567,10 +582,10 @@ struct TileEngine {
                         uint16_t* dst = p.o + (int64_t)(p0 + r) * p.H + n0;
                         if constexpr (C::NT == 8) {
                             uint4 v;
-                            v.x = f32_to_bf16(acc[mt][0][i]) | (f32_to_bf16(acc[mt][1][i]) << 16);
-                            v.y = f32_to_bf16(acc[mt][2][i]) | (f32_to_bf16(acc[mt][3][i]) << 16);
-                            v.z = f32_to_bf16(acc[mt][4][i]) | (f32_to_bf16(acc[mt][5][i]) << 16);
-                            v.w = f32_to_bf16(acc[mt][6][i]) | (f32_to_bf16(acc[mt][7][i]) << 16);
+                            v.x = pack_bf16x2(acc[mt][0][i], acc[mt][1][i]);
+                            v.y = pack_bf16x2(acc[mt][2][i], acc[mt][3][i]);
+                            v.z = pack_bf16x2(acc[mt][4][i], acc[mt][5][i]);
+                            v.w = pack_bf16x2(acc[mt][6][i], acc[mt][7][i]);
                             *reinterpret_cast<uint4*>(dst) = v;
                         } else {
 #pragma unroll
