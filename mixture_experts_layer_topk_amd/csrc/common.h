@@ -53,12 +53,13 @@ MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
 // log2 of Q's binade (8 for 448, 2 for 6).
 template <uint32_t kMantThresh, int kShift>
 MOE_DEV int block_exp(float amax) {
-    uint32_t a = f2u(amax) & 0x7FFFFFFFu;
-    if (a == 0) return 0;
-    int E = (int)(a >> 23) - 127;
-    if ((a >> 23) == 0) return -127;               // float32 subnormal: below E8M0 range
-    int e = E - kShift + ((a & 0x7FFFFFu) > kMantThresh ? 1 : 0);
-    return e < -127 ? -127 : (e > 127 ? 127 : e);
+    // selects rather than early returns: no divergent branches in the epilogues
+    const uint32_t a = f2u(amax) & 0x7FFFFFFFu;
+    const int biased = (int)(a >> 23);
+    int e = biased - 127 - kShift + ((a & 0x7FFFFFu) > kMantThresh ? 1 : 0);
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    // zero: 0; a float32 subnormal lies below the E8M0 range: -127
+    return biased == 0 ? (a == 0 ? 0 : -127) : e;
 }
 MOE_DEV int e4m3_block_exp(float amax) { return block_exp<0x600000u, 8>(amax); }
 MOE_DEV int e2m1_block_exp(float amax) { return block_exp<0x400000u, 2>(amax); }

@@ -155,14 +155,12 @@ MOE_DEV int scale_slot_row(int q) { return (q & ~63) | ((q & 3) << 4) | ((q >> 2
 // Largest value over each group of 8 neighbouring lanes (lanes 8j .. 8j + 7),
 // with DPP row operations instead of LDS round trips: swap neighbours, swap
 // pairs (each quad then holds its maximum), then mirror the 8-lane half-row
-// (quad 0 meets quad 1).  Inputs are finite.
-MOE_DEV float max_of_8_lanes(float v) {
-    float m = __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-    v = v > m ? v : m;
-    m = __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xF, 0xF, false);         // quad_perm [2,3,0,1]
-    v = v > m ? v : m;
-    m = __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xF, 0xF, false);        // row_half_mirror
-    return v > m ? v : m;
+// (quad 0 meets quad 1).  The values are bit patterns of non-negative floats,
+// which order like the unsigned integers.
+MOE_DEV uint32_t max_of_8_lanes(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));  // half mirror
 }
 
 // kAux: cache policy bits of the load (kCohAux: device-coherent, sc1)
@@ -519,6 +517,14 @@ struct TileEngine {
             constexpr int QN = C::NT / 2;
             static_assert(QN == 4, "a 32-column E4M3 group is 8 neighbouring lanes");
             const int icol0 = ntile * (BN / 2) + L.wn * (C::WTN / 2);
+            const int col = icol0 + L.l16 * QN;
+            // this lane's first row (m-tile 0, i = 0): the stores of row
+            // mt * 16 + i below add (mt * 16 + i) * I (codes) or * 4 (scales)
+            const int r0 = L.wm * C::WTM + 4 * L.lg;
+            const int64_t pos0 = (int64_t)p0 + r0;
+            uint8_t* hq_lane = p.hq + pos0 * p.I + col;
+            uint8_t* hsf_lane = p.hsf + (int64_t)(col / (4 * kGroup)) * (p.T * p.topk) * 4 + pos0 * 4 +
+                                (col / kGroup) % 4;
 #pragma unroll
             for (int mt = 0; mt < C::MT; ++mt) {
                 // one m-tile at a time: bounds the registers live in the epilogue
@@ -531,20 +537,17 @@ struct TileEngine {
                     const int r = L.wm * C::WTM + mt * 16 + 4 * L.lg + i;
                     const float wr = wrow[i];
                     float h[QN];
-                    float amax = 0.f;
+                    uint32_t amax = 0;              // bits of max |h| (finite)
 #pragma unroll
                     for (int q = 0; q < QN; ++q) {
                         const float g = acc[mt][2 * q][i], u = acc[mt][2 * q + 1][i];
                         h[q] = swiglu_w(g, u, wr);
-                        amax = fmaxf(amax, __builtin_fabsf(h[q]));
+                        amax = max(amax, f2u(h[q]) & 0x7FFFFFFFu);
                     }
-                    amax = max_of_8_lanes(amax);
-                    const int ex = e4m3_block_exp(amax);
+                    const int ex = e4m3_block_exp(u2f(max_of_8_lanes(amax)));
                     const float inv = exp2_neg(ex);
-                    const int col = icol0 + L.l16 * QN;
                     if (r < valid && col < p.I) {
-                        const int64_t pos = p0 + r;
-                        uint8_t* dst = p.hq + pos * p.I + col;
+                        uint8_t* dst = hq_lane + (int64_t)(mt * 16 + i) * p.I;
                         static_assert(QN % 4 == 0, "whole dwords of E4M3 codes per lane");
 #pragma unroll
                         for (int q = 0; q < QN; q += 4) {
@@ -557,8 +560,7 @@ struct TileEngine {
                                 *d = v;
                         }
                         if ((col & (kGroup - 1)) == 0) {
-                            uint8_t* d = p.hsf + (int64_t)(col / (4 * kGroup)) * (p.T * p.topk) * 4 +
-                                         pos * 4 + (col / kGroup) % 4;
+                            uint8_t* d = hsf_lane + (mt * 16 + i) * 4;
                             if constexpr (kCoh)
                                 __hip_atomic_store(d, (uint8_t)(ex + 127), __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
