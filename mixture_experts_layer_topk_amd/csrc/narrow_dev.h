@@ -76,6 +76,62 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
     };
 
     for (int u0 = bid; u0 < nunits; u0 += kBatch * G) {
+        const int nb = min(kBatch, (nunits - u0 + G - 1) / G);
+        const int nitems = nb * nchunk;
+
+        // ---- item q: unit q / nchunk, K steps kb + (q % nchunk) * KC + [0, KC)
+        // Items past the end re-read the last one (cached) and K steps past the
+        // wave's range re-read one inside it, so every path issues the same loads
+        // and the compiler's counted waits keep the later buffers in flight.
+        // Weights (expert e, column chunk nc) and activations are issued apart:
+        // the first items' weights go out as soon as their expert is known,
+        // before the unit headers (rows, routing weights) are resolved.
+        auto issue_w = [&](NarrowBuf<KC>& bf, int q, int e, int nc) {
+            q = min(q, nitems - 1);
+            const int c = q % nchunk;
+            const uint8_t* wq_e = wq + (int64_t)e * wrows * (K / 2) + lg * 16;
+            const uint8_t* wsf_e = wsf + (int64_t)e * nk * w_slab;
+#pragma unroll
+            for (int jj = 0; jj < KC; ++jj) {
+                const int ks = max(0, min(kb + c * KC + jj, min(ke, nk) - 1));
+#pragma unroll
+                for (int t = 0; t < kNT; ++t) {
+                    const int br = brow(nc, t);
+                    bf.b[jj][t] = *reinterpret_cast<const v4i*>(wq_e + (int64_t)br * (K / 2) +
+                                                                ks * (kKStep / 2));
+                    bf.sb[jj][t] = *reinterpret_cast<const uint32_t*>(wsf_e + ks * w_slab + br * 4);
+                }
+            }
+        };
+        auto issue_a = [&](NarrowBuf<KC>& bf, int q) {
+            q = min(q, nitems - 1);
+            const int j = q / nchunk, c = q - j * nchunk;
+            const int64_t arow = s_arow[j][l16];
+            const uint8_t* ap = aq + arow * K + lg * 16;
+            const uint8_t* asp = asf + arow * 4;
+#pragma unroll
+            for (int jj = 0; jj < KC; ++jj) {
+                const int ks = max(0, min(kb + c * KC + jj, min(ke, nk) - 1));
+                bf.alo[jj] = *reinterpret_cast<const v4i*>(ap + ks * kKStep);
+                bf.ahi[jj] = *reinterpret_cast<const v4i*>(ap + ks * kKStep + 64);
+                bf.sa[jj] = *reinterpret_cast<const uint32_t*>(asp + ks * a_slab);
+            }
+        };
+        auto issue = [&](NarrowBuf<KC>& bf, int q) {
+            const int j = min(q, nitems - 1) / nchunk;
+            issue_w(bf, q, s_hdr[j][0], s_hdr[j][3]);
+            issue_a(bf, q);
+        };
+
+        NarrowBuf<KC> buf[NBUF];
+        // the first items' weights: expert from the sub-tile record directly
+#pragma unroll
+        for (int q = 0; q < NBUF - 1; ++q) {
+            const int u = u0 + (min(q, nitems - 1) / nchunk) * G;
+            const int m = u / nch;
+            issue_w(buf[q], q, p.sub_rec[m].x, u - m * nch);
+        }
+
         // ---- headers of units u0 + j * G, j < kBatch (16 threads per unit)
         __syncthreads();                                // the previous batch is done with LDS
         {
@@ -103,37 +159,6 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
             }
         }
         __syncthreads();
-        const int nb = min(kBatch, (nunits - u0 + G - 1) / G);
-        const int nitems = nb * nchunk;
-
-        // ---- item q: unit q / nchunk, K steps kb + (q % nchunk) * KC + [0, KC)
-        // Items past the end re-read the last one (cached) and K steps past the
-        // wave's range re-read one inside it, so every path issues the same loads
-        // and the compiler's counted waits keep the later buffers in flight.
-        auto issue = [&](NarrowBuf<KC>& bf, int q) {
-            q = min(q, nitems - 1);
-            const int j = q / nchunk, c = q - j * nchunk;
-            const int e = s_hdr[j][0], nc = s_hdr[j][3];
-            const int64_t arow = s_arow[j][l16];
-            const uint8_t* wq_e = wq + (int64_t)e * wrows * (K / 2) + lg * 16;
-            const uint8_t* wsf_e = wsf + (int64_t)e * nk * w_slab;
-            const uint8_t* ap = aq + arow * K + lg * 16;
-            const uint8_t* asp = asf + arow * 4;
-#pragma unroll
-            for (int jj = 0; jj < KC; ++jj) {
-                const int ks = max(0, min(kb + c * KC + jj, min(ke, nk) - 1));
-#pragma unroll
-                for (int t = 0; t < kNT; ++t) {
-                    const int br = brow(nc, t);
-                    bf.b[jj][t] = *reinterpret_cast<const v4i*>(wq_e + (int64_t)br * (K / 2) +
-                                                                ks * (kKStep / 2));
-                    bf.sb[jj][t] = *reinterpret_cast<const uint32_t*>(wsf_e + ks * w_slab + br * 4);
-                }
-                bf.alo[jj] = *reinterpret_cast<const v4i*>(ap + ks * kKStep);
-                bf.ahi[jj] = *reinterpret_cast<const v4i*>(ap + ks * kKStep + 64);
-                bf.sa[jj] = *reinterpret_cast<const uint32_t*>(asp + ks * a_slab);
-            }
-        };
 
         v4f acc[kNT];
         auto epilogue = [&](int j) {
@@ -213,9 +238,8 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
             if (c == nchunk - 1) epilogue(j);
         };
 
-        NarrowBuf<KC> buf[NBUF];
 #pragma unroll
-        for (int q = 0; q < NBUF - 1; ++q) issue(buf[q], q);
+        for (int q = 0; q < NBUF - 1; ++q) issue_a(buf[q], q);
         for (int q0 = 0; q0 < nitems; q0 += NBUF) {
 #pragma unroll
             for (int b = 0; b < NBUF; ++b) {
