@@ -70,8 +70,8 @@ __global__ __launch_bounds__(kLayerThreads) void layer_small_kernel(RouteParams 
                                                                     GemmParams gp, LayerParams lp) {
     const int G = gridDim.x, bid = blockIdx.x;
     // phase 1: workgroup 0 routes and buckets, the others quantise x
-    if (bid == 0) bucket_small(rp, sp, lp.npl);
-    if (rp.x && (bid > 0 || G == 1)) quant_rows(rp, G > 1 ? bid - 1 : 0, G > 1 ? G - 1 : 1);
+    if (bid == 0) bucket_small<kLayerThreads>(rp, sp, lp.npl);
+    if (rp.x && (bid > 0 || G == 1)) quant_rows<kLayerThreads>(rp, G > 1 ? bid - 1 : 0, G > 1 ? G - 1 : 1);
     grid_barrier(lp.count, (unsigned)G, lp.status);
     narrow_gemm<true>(gp, bid, G);
     grid_barrier(lp.count, 2u * G, lp.status);

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_quant_kernel(RouteP
         route_count_block(p, npl);
         return;
     }
-    if (p.x) quant_rows(p, (int)blockIdx.x - route_blocks, (int)gridDim.x - route_blocks);
+    if (p.x) quant_rows<kRouteThreads>(p, (int)blockIdx.x - route_blocks, (int)gridDim.x - route_blocks);
 }
 
 __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p) {
@@ -73,25 +73,25 @@ __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p)
 
 // Few pairs (T * k <= kSmallPairs): workgroup 0 routes and buckets every pair
 // with no second launch; the other workgroups quantise x meanwhile.
-__global__ __launch_bounds__(kRouteThreads) void route_small_kernel(RouteParams rp, ScatterParams sp,
+__global__ __launch_bounds__(kSmallThreads) void route_small_kernel(RouteParams rp, ScatterParams sp,
                                                                     int npl) {
     if (blockIdx.x == 0) {
-        bucket_small(rp, sp, npl);
+        bucket_small<kSmallThreads>(rp, sp, npl);
         if (gridDim.x > 1) return;                    // the other workgroups quantise x
     }
     if (rp.x) {
         const int b = gridDim.x > 1 ? (int)blockIdx.x - 1 : 0;
-        quant_rows(rp, b, gridDim.x > 1 ? (int)gridDim.x - 1 : 1);
+        quant_rows<kSmallThreads>(rp, b, gridDim.x > 1 ? (int)gridDim.x - 1 : 1);
     }
 }
 
 hipError_t launch_route(const RouteParams& rp, const ScatterParams& sp, hipStream_t s) {
     if (rp.T > 0 && rp.T * rp.topk <= kSmallPairs) {
         // workgroup 0 routes and buckets; the others quantise x
-        int64_t quant_blocks = rp.x ? (rp.T * (rp.H / 8) + 2 * kRouteThreads - 1) / (2 * kRouteThreads) : 0;
+        int64_t quant_blocks = rp.x ? (rp.T * (rp.H / 8) + kSmallThreads - 1) / kSmallThreads : 0;
         dim3 grid((unsigned)(1 + std::min<int64_t>(quant_blocks, 2048)));
         const int npl = rp.logits ? (rp.E + 63) / 64 : 1;
-        hipLaunchKernelGGL(route_small_kernel, grid, dim3(kRouteThreads), 0, s, rp, sp, npl);
+        hipLaunchKernelGGL(route_small_kernel, grid, dim3(kSmallThreads), 0, s, rp, sp, npl);
         return hipGetLastError();
     }
     if (rp.T > 0) {

@@ -10,10 +10,10 @@
 namespace moe {
 
 constexpr int kRouteThreads = 256;
-constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kMaxTopk = 16;
 constexpr int kMaxExperts = kMaxExpertsCap;
 constexpr int kSmallPairs = 1024;       // T * k up to which one workgroup buckets every pair
+constexpr int kSmallThreads = 512;      // that workgroup's size: one wave per token up to 8 tokens
 
 // Unsigned integer with the order of the float value (finite inputs); -0 and
 // +0 map to the same integer, as they compare equal.
@@ -33,77 +33,81 @@ MOE_DEV void load_logits(const float* __restrict__ lrow, int E, float (&v)[NPL])
     }
 }
 
+// Largest (smallest) of x over the 64 lanes of a fully active wave, in every
+// lane: butterflies inside each row of 16 lanes by DPP (lane pairs 1 apart, 2
+// apart, then the mirrored halves of 8 and of 16), then the four row results
+// through scalar registers.
+MOE_DEV uint32_t row_max_u32(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));
+    return max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));
+}
+MOE_DEV uint32_t wave_max_u32(uint32_t x) {
+    x = row_max_u32(x);
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)x, 0),
+                           (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)x, 32),
+                           (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+    return max(a, b);
+}
+MOE_DEV uint32_t wave_min_u32(uint32_t x) { return ~wave_max_u32(~x); }
+
 // Top-k of one token's E logits with one wave.  Lane l owns experts
 // l, l + 64, ...; NPL = values per lane.  Writes idx/w for the token.
 //
-// Every expert gets a unique 42-bit key, its float order in the high bits and
-// 1023 - e in the low 10, so a larger key means a larger logit, or an equal
-// logit and a smaller index (the tie rule).  The k-th largest key T is found
-// bit by bit from the top: a candidate bit is kept when at least k keys are
-// >= the candidate, each count a ballot and a popcount per value slot (no LDS
-// traffic).  The k keys >= T are then compacted into LDS and each is ranked
-// by the number of selected keys above it, which orders the slots.
+// k rounds of a wave-wide argmax.  Each lane compares its remaining logits
+// by float order (the larger logit wins, the smaller index on equal logits),
+// the wave takes the largest order value, and of the lanes that hold it the
+// one with the smallest expert index wins (a single lane nearly always; a
+// second reduction otherwise).  The winner leaves its lane's candidates, and
+// lane j keeps round j's expert and logit, so the k slots come out ordered
+// by decreasing logit, smaller index first among equal logits.
 template <int NPL>
 MOE_DEV void route_token(const float (&v)[NPL], int E, int k, int score_fn, int renorm,
-                         int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-                         float* sel_v, int* sel_i, uint64_t* sel_k, int* lds_idx) {
+                         int32_t* __restrict__ idx_out, float* __restrict__ w_out, int* lds_idx) {
     const int lane = threadIdx.x & 63;
-    uint64_t key[NPL];
+    uint32_t ord[NPL];                      // 0: no expert here, or already taken
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = e < E ? ((uint64_t)float_order(v[i]) << 10) | (uint64_t)(1023 - e) : 0;
-    }
-    uint64_t T = 0;
-    for (int bit = 41; bit >= 0; --bit) {
-        const uint64_t c = T | (1ull << bit);
-        int cnt = 0;
+    for (int i = 0; i < NPL; ++i) ord[i] = lane + 64 * i < E ? float_order(v[i]) : 0u;
+    int my_e = 0;
+    float my_v = 0.0f, lmax = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        uint32_t best = ord[0];
+        int bi = 0;
+        float bv = v[0];
 #pragma unroll
-        for (int i = 0; i < NPL; ++i) cnt += __popcll(__ballot(key[i] >= c));
-        if (cnt >= k) T = c;
-    }
-    // compact the k selected keys (and their logits) into LDS
-    int base = 0;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const bool sel = key[i] >= T;
-        const uint64_t m = __ballot(sel);
-        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (sel) {
-            sel_k[base + below] = key[i];
-            sel_v[base + below] = v[i];
+        for (int i = 1; i < NPL; ++i) {
+            if (ord[i] > best) {
+                best = ord[i];
+                bi = i;
+                bv = v[i];
+            }
         }
-        base += __popcll(m);
+        const uint32_t m = wave_max_u32(best);
+        const uint64_t tied = __ballot(best == m);
+        int e;
+        if (__popcll(tied) == 1) {
+            const int wl = __builtin_ctzll(tied);
+            e = wl + 64 * __builtin_amdgcn_readlane(bi, wl);
+        } else {
+            e = (int)wave_min_u32(best == m ? (uint32_t)(lane + 64 * bi) : ~0u);
+        }
+        // expert e is its lane's best candidate, so that lane's bv is its logit
+        const float ev = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), e & 63));
+        if (j == 0) lmax = ev;
+        if (lane == j) {
+            my_e = e;
+            my_v = ev;
+        }
+#pragma unroll
+        for (int i = 0; i < NPL; ++i)
+            if (lane + 64 * i == e) ord[i] = 0u;
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    uint64_t x = 0;
-    float xv = 0.0f;
-    int rank = 0;
-    if (lane < k) {
-        x = sel_k[lane];
-        xv = sel_v[lane];
-        for (int j = 0; j < k; ++j) rank += sel_k[j] > x;
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (lane < k) {
-        sel_v[rank] = xv;
-        sel_i[rank] = 1023 - (int)(x & 1023);
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // weights
-    float lmax = sel_v[0];
     float s = 0.0f;
-    if (lane < k) {
-        float lv = sel_v[lane];
-        s = score_fn == 0 ? expf(lv - lmax) : 1.0f / (1.0f + expf(-lv));
-    }
+    if (lane < k) s = score_fn == 0 ? expf(my_v - lmax) : 1.0f / (1.0f + expf(-my_v));
     float denom = 1.0f;
     if (renorm) {
         denom = wave_sum(s);
@@ -115,18 +119,20 @@ MOE_DEV void route_token(const float (&v)[NPL], int E, int k, int score_fn, int 
         denom = wave_sum(z);
     }
     if (lane < k) {
-        idx_out[lane] = sel_i[lane];
-        lds_idx[lane] = sel_i[lane];
+        idx_out[lane] = my_e;
+        lds_idx[lane] = my_e;
         w_out[lane] = s / denom;
     }
 }
 
-// Quantise x rows [T, H]: task i covers 8 elements of the flattened array.
+// Quantise x rows [T, H]: task i covers 8 elements of the flattened array;
+// workgroups of kThreads threads.
+template <int kThreads>
 MOE_DEV void quant_rows(const RouteParams& p, int block, int nblocks) {
     const int64_t tasks = p.T * (p.H / 8);
-    const int64_t stride = (int64_t)nblocks * kRouteThreads;
+    const int64_t stride = (int64_t)nblocks * kThreads;
     constexpr int U = 4;
-    for (int64_t i0 = (int64_t)block * kRouteThreads + threadIdx.x; i0 < tasks; i0 += U * stride) {
+    for (int64_t i0 = (int64_t)block * kThreads + threadIdx.x; i0 < tasks; i0 += U * stride) {
         uint4 raw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -164,38 +170,48 @@ MOE_DEV void quant_rows(const RouteParams& p, int block, int nblocks) {
     }
 }
 
-// The tokens [t0, t0 + ntok) of this wave: i = wave, wave + kRouteWaves, ...
-template <int NPL>
-MOE_DEV void route_tokens(const RouteParams& p, int64_t t0, int ntok, int* pair_exp, float* sel_v,
-                          int* sel_i, uint64_t* sel_k) {
+// The tokens [t0, t0 + ntok) of this wave: i = wave, wave + W, ... for a
+// workgroup of W waves.  Up to 4 logits per lane, the next token's logits are
+// loaded while the current one is routed (more would cost registers that the
+// quantising workgroups of the same kernel need for occupancy).
+template <int NPL, int kThreads>
+MOE_DEV void route_tokens(const RouteParams& p, int64_t t0, int ntok, int* pair_exp) {
+    constexpr int W = kThreads / 64;
+    constexpr bool kPrefetch = NPL <= 4;
     const int k = p.topk;
     int i = threadIdx.x >> 6;
     if (i >= ntok) return;
-    float v[NPL];
-    for (; i < ntok; i += kRouteWaves) {
+    float v[NPL], nv[NPL];
+    if (kPrefetch) load_logits<NPL>(p.logits + (t0 + i) * p.E, p.E, v);
+    for (; i < ntok; i += W) {
         const int64_t t = t0 + i;
-        load_logits<NPL>(p.logits + t * p.E, p.E, v);
-        route_token<NPL>(v, p.E, k, p.score_fn, p.renorm, p.idx_out + t * k, p.w_out + t * k, sel_v,
-                         sel_i, sel_k, pair_exp + i * k);
+        if (kPrefetch)
+            load_logits<NPL>(p.logits + (t0 + min(i + W, ntok - 1)) * p.E, p.E, nv);
+        else
+            load_logits<NPL>(p.logits + t * p.E, p.E, v);
+        route_token<NPL>(v, p.E, k, p.score_fn, p.renorm, p.idx_out + t * k, p.w_out + t * k,
+                         pair_exp + i * k);
+        if (kPrefetch) {
+#pragma unroll
+            for (int j = 0; j < NPL; ++j) v[j] = nv[j];
+        }
     }
 }
 
 // Route tokens [t0, t0 + ntok) (one wave per token) or take the caller's ids;
 // pair i = (t - t0) * k + j of the chunk gets its expert in pair_exp[i].
-MOE_DEV void route_chunk(const RouteParams& p, int64_t t0, int ntok, int npl, int* pair_exp,
-                         float (*sel_v)[kMaxTopk], int (*sel_i)[kMaxTopk],
-                         uint64_t (*sel_k)[kMaxTopk]) {
+template <int kThreads>
+MOE_DEV void route_chunk(const RouteParams& p, int64_t t0, int ntok, int npl, int* pair_exp) {
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
     const int k = p.topk;
     if (p.logits) {
-        if (npl <= 1) route_tokens<1>(p, t0, ntok, pair_exp, sel_v[wave], sel_i[wave], sel_k[wave]);
-        else if (npl <= 2) route_tokens<2>(p, t0, ntok, pair_exp, sel_v[wave], sel_i[wave], sel_k[wave]);
-        else if (npl <= 4) route_tokens<4>(p, t0, ntok, pair_exp, sel_v[wave], sel_i[wave], sel_k[wave]);
-        else if (npl <= 8) route_tokens<8>(p, t0, ntok, pair_exp, sel_v[wave], sel_i[wave], sel_k[wave]);
-        else route_tokens<16>(p, t0, ntok, pair_exp, sel_v[wave], sel_i[wave], sel_k[wave]);
+        if (npl <= 1) route_tokens<1, kThreads>(p, t0, ntok, pair_exp);
+        else if (npl <= 2) route_tokens<2, kThreads>(p, t0, ntok, pair_exp);
+        else if (npl <= 4) route_tokens<4, kThreads>(p, t0, ntok, pair_exp);
+        else if (npl <= 8) route_tokens<8, kThreads>(p, t0, ntok, pair_exp);
+        else route_tokens<16, kThreads>(p, t0, ntok, pair_exp);
     } else {
-        for (int i = tid; i < ntok * k; i += kRouteThreads) {
+        for (int i = tid; i < ntok * k; i += kThreads) {
             int e = p.idx_in[t0 * k + i];
             pair_exp[i] = e;
             if (p.idx_in != p.idx_out) {
@@ -206,13 +222,18 @@ MOE_DEV void route_chunk(const RouteParams& p, int64_t t0, int ntok, int npl, in
     }
 }
 
+// Workgroup barrier that orders LDS accesses only: global stores issued
+// before it need not have completed (nothing in this workgroup reads them back).
+MOE_DEV void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Routing and counting of one chunk of kRouteTokensPerBlock tokens.
 MOE_DEV void route_count_block(const RouteParams& p, int npl) {
     __shared__ int hist[kMaxExperts];
     __shared__ int base[kMaxExperts];
-    __shared__ float sel_v[kRouteWaves][kMaxTopk];
-    __shared__ int sel_i[kRouteWaves][kMaxTopk];
-    __shared__ uint64_t sel_k[kRouteWaves][kMaxTopk];
     __shared__ int pair_rank[kRouteTokensPerBlock * kMaxTopk];
     __shared__ int pair_exp[kRouteTokensPerBlock * kMaxTopk];   // expert of pair i of this block
 
@@ -223,8 +244,8 @@ MOE_DEV void route_count_block(const RouteParams& p, int npl) {
 
     for (int e = tid; e < p.E; e += kRouteThreads) hist[e] = 0;
     // 1. routing (one wave per token) or caller's ids
-    route_chunk(p, t0, ntok, npl, pair_exp, sel_v, sel_i, sel_k);
-    __syncthreads();
+    route_chunk<kRouteThreads>(p, t0, ntok, npl, pair_exp);
+    lds_barrier();
 
     // 2. count: LDS histogram; the LDS atomic's return is the pair's rank here
     const int npairs = ntok * k;
@@ -232,12 +253,12 @@ MOE_DEV void route_count_block(const RouteParams& p, int npl) {
         int e = pair_exp[i];
         pair_rank[i] = (e >= 0 && e < p.E) ? atomicAdd(&hist[e], 1) : -1;
     }
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < p.E; e += kRouteThreads) {
         int c = hist[e];
         base[e] = c ? atomicAdd(&p.cnt[e], c) : 0;
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < npairs; i += kRouteThreads) {
         int e = pair_exp[i];
         p.slot_in_e[t0 * k + i] = pair_rank[i] >= 0 ? base[e] + pair_rank[i] : -1;
@@ -317,36 +338,78 @@ MOE_DEV void write_tables(const ScatterParams& p, const int* cnt, const int* off
     }
 }
 
-
 // Few pairs (T * k <= kSmallPairs), one workgroup: route every token, count
 // the pairs in an LDS histogram whose atomic returns each pair's rank inside
 // its expert, scan the counts, scatter the pairs and write the tables, with no
 // global counters ("05.10 Counting Sort / Bucketization" 2.1-2.3 inside one
-// workgroup).
+// workgroup).  One scan serves the pair offsets and both tile tables: each
+// expert contributes its pairs, m-tiles and sub-tiles as three 21-bit fields
+// of one 64-bit value (none of the sums reaches 2^21 at this size), and the
+// thread that owns an expert writes that expert's records itself.  Workgroups
+// of kThreads threads.
+template <int kThreads>
 MOE_DEV void bucket_small(const RouteParams& rp, const ScatterParams& sp, int npl) {
+    using Scan = rocprim::block_scan<uint64_t, kThreads>;
+    constexpr int kPer = kMaxExperts / kThreads;          // experts per thread
+    constexpr uint64_t kField = (1u << 21) - 1;
     __shared__ int hist[kMaxExperts];
-    __shared__ int off[kMaxExperts + 1];
-    __shared__ int tiles[kMaxExperts];
-    __shared__ int toff[kMaxExperts + 1];
-    __shared__ BlockScan::storage_type tmp;
-    __shared__ float sel_v[kRouteWaves][kMaxTopk];
-    __shared__ int sel_i[kRouteWaves][kMaxTopk];
-    __shared__ uint64_t sel_k[kRouteWaves][kMaxTopk];
+    __shared__ int off[kMaxExperts];
+    __shared__ typename Scan::storage_type tmp;
     __shared__ int pair_exp[kSmallPairs];
     __shared__ int pair_rank[kSmallPairs];
     const int tid = threadIdx.x;
-    const int k = rp.topk;
+    const int k = rp.topk, E = rp.E, bm = sp.bm;
     const int npairs = (int)rp.T * k;
-    for (int e = tid; e < rp.E; e += kRouteThreads) hist[e] = 0;
-    route_chunk(rp, 0, (int)rp.T, npl, pair_exp, sel_v, sel_i, sel_k);
-    __syncthreads();
-    for (int i = tid; i < npairs; i += kRouteThreads) {
+    for (int e = tid; e < E; e += kThreads) hist[e] = 0;
+    route_chunk<kThreads>(rp, 0, (int)rp.T, npl, pair_exp);
+    lds_barrier();
+    for (int i = tid; i < npairs; i += kThreads) {
         const int e = pair_exp[i];
-        pair_rank[i] = (e >= 0 && e < rp.E) ? atomicAdd(&hist[e], 1) : -1;
+        pair_rank[i] = (e >= 0 && e < E) ? atomicAdd(&hist[e], 1) : -1;
     }
-    __syncthreads();
-    block_exclusive_scan(hist, off, rp.E, tmp);
-    for (int i = tid; i < npairs; i += kRouteThreads) {
+    lds_barrier();
+    int c[kPer];
+    uint64_t f[kPer], x[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int e = tid * kPer + j;
+        c[j] = e < E ? hist[e] : 0;
+        f[j] = (uint64_t)c[j] | (uint64_t)ceil_div(c[j], bm) << 21 |
+               (uint64_t)ceil_div(c[j], kSubRows) << 42;
+    }
+    uint64_t total;
+    Scan().exclusive_scan(f, x, (uint64_t)0, total, tmp);
+    const int n_mtiles = (int)((total >> 21) & kField), n_subs = (int)(total >> 42);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int e = tid * kPer + j;
+        if (e >= E) break;
+        const int o = (int)(x[j] & kField);
+        int m = (int)((x[j] >> 21) & kField), u = (int)(x[j] >> 42);
+        off[e] = o;
+        sp.counts_out[e] = c[j];
+        sp.offsets_out[e] = o;
+        sp.mtile_off[e] = m;
+        for (int r = 0; r < c[j]; r += bm, ++m) {
+            sp.mtile_rec[m] = make_int4(e, o + r, min(bm, c[j] - r), 0);
+            sp.mtile_e[m] = e;
+        }
+        for (int r = 0; r < c[j]; r += kSubRows, ++u)
+            sp.sub_rec[u] = make_int4(e, o + r, min(kSubRows, c[j] - r), 0);
+    }
+    if (tid == 0) {
+        sp.offsets_out[E] = (int)(total & kField);
+        sp.mtile_off[E] = n_mtiles;
+        *sp.nsub = n_subs;
+        *sp.status = 0;
+    }
+    // records past the last tile are zero; the one-launch GEMMs' counters start at zero
+    const int4 zero = make_int4(0, 0, 0, 0);
+    for (int m = n_mtiles + tid; m < sp.max_mtiles; m += kThreads) sp.mtile_rec[m] = zero;
+    for (int m = n_subs + tid; m < sp.max_subs; m += kThreads) sp.sub_rec[m] = zero;
+    for (int m = tid; m < sp.max_mtiles; m += kThreads) sp.ready[m] = 0;
+    lds_barrier();                                        // off[] complete
+    for (int i = tid; i < npairs; i += kThreads) {
         const int e = pair_exp[i];
         if (pair_rank[i] >= 0) {
             const int pos = off[e] + pair_rank[i];
@@ -356,7 +419,6 @@ MOE_DEV void bucket_small(const RouteParams& rp, const ScatterParams& sp, int np
             sp.slot_of[i] = -1;
         }
     }
-    write_tables(sp, hist, off, tiles, toff, tmp, 0, 1);
 }
 
 }  // namespace moe
