@@ -95,6 +95,15 @@ MOE_DEV uint32_t e2m1_encode(float x) {
 
 MOE_DEV int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Workgroup barrier that orders LDS accesses only: global memory operations
+// issued before it need not have completed (for phases in which no wave reads
+// back what another wrote to global memory).
+MOE_DEV void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wave-level reductions over 64 lanes.
 MOE_DEV float wave_max(float v) {
 #pragma unroll

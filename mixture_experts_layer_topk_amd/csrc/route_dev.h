@@ -222,14 +222,6 @@ MOE_DEV void route_chunk(const RouteParams& p, int64_t t0, int ntok, int npl, in
     }
 }
 
-// Workgroup barrier that orders LDS accesses only: global stores issued
-// before it need not have completed (nothing in this workgroup reads them back).
-MOE_DEV void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Routing and counting of one chunk of kRouteTokensPerBlock tokens.
 MOE_DEV void route_count_block(const RouteParams& p, int npl) {
     __shared__ int hist[kMaxExperts];
