@@ -22,7 +22,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Carve {
     size_t cnt, arrive, status, counts, offsets, mtile_off, mtile_e, mtile_rec, sub_rec, nsub, ready,
-        topk_idx, topk_w, slot_in_e, slot_src, slot_of;
+        topk_idx, topk_w, slot_in_e, slot_src, slot_of, slot_w;
     size_t xq, xsf, hq, hsf, o, total;
 };
 
@@ -62,6 +62,7 @@ Carve carve(const moe_dims_t& d) {
     c.slot_in_e = take(R * 4);
     c.slot_src = take(R * 4);
     c.slot_of = take(R * 4);
+    c.slot_w = take(R * 4);
     c.xq = take(T * (size_t)d.H);
     c.xsf = take(T * (size_t)d.H / 32);
     c.hq = take(R * (size_t)d.I);
@@ -172,6 +173,8 @@ int moe_route(const moe_dims_t* d, const float* logits, int32_t* topk_idx, float
     sp.mtile_e = at<int32_t>(ws, c.mtile_e);
     sp.slot_src = slot_src;
     sp.slot_of = slot_of;
+    sp.wts = topk_w;
+    sp.slot_w = at<float>(ws, c.slot_w);
     sp.T = d->T;
     sp.E = d->E;
     sp.topk = d->topk;
@@ -263,6 +266,8 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     sp.mtile_e = at<int32_t>(ws, c.mtile_e);
     sp.slot_src = at<int32_t>(ws, c.slot_src);
     sp.slot_of = at<int32_t>(ws, c.slot_of);
+    sp.wts = rp.w_out;
+    sp.slot_w = at<float>(ws, c.slot_w);
     sp.T = d.T;
     sp.E = d.E;
     sp.topk = d.topk;
@@ -290,6 +295,7 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     gp.ready = at<int>(ws, c.ready);
     gp.status = at<int>(ws, c.status);
     gp.slot_src = sp.slot_src;
+    gp.slot_w = sp.slot_w;
     gp.topk_w = rp.w_out;
     gp.xq = rp.xq;
     gp.xsf = rp.xsf;

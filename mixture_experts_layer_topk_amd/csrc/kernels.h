@@ -44,6 +44,8 @@ struct ScatterParams {
     int* status;                // [1] zeroed here
     int32_t* slot_src;          // [T*k]
     int32_t* slot_of;           // [T, k]
+    const float* wts;           // [T, k] routing weights (read by the multi-workgroup scatter)
+    float* slot_w;              // [T*k] routing weight of the pair at each position
     int64_t T;
     int E, topk, bm, max_mtiles, max_subs;
 };
@@ -67,6 +69,7 @@ struct GemmParams {
     const int4* sub_rec;        // [max_subs] the same for 16-row sub-tiles
     const int32_t* nsub;        // [1] number of 16-row sub-tiles
     const int32_t* slot_src;    // [R] t*k + j of position p
+    const float* slot_w;        // [R] routing weight of the pair at position p
     const float* topk_w;        // [T, k]
     const uint8_t* xq;          // [T, H]    GEMM1 A (gathered rows)
     const uint8_t* xsf;         // [H/128, T, 4]      K-step major scales

@@ -123,42 +123,46 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
             issue_a(bf, q);
         };
 
+        // This thread's unit header (16 threads per unit) and the experts of the
+        // first items are read before any weight load goes out, and so are the
+        // unit rows' pair ids and routing weights (GEMM1): loads complete in
+        // issue order, so anything issued after the weights would wait for them.
+        const int hj = tid / kSubRows, hr = tid % kSubRows;
+        const int hu = u0 + hj * G;
+        int4 hrec = make_int4(0, 0, 1, 0);
+        if (hu < nunits) hrec = p.sub_rec[hu / nch];    // {expert, first position, rows}
+        int early_e[NBUF - 1];
+#pragma unroll
+        for (int q = 0; q < NBUF - 1; ++q)
+            early_e[q] = p.sub_rec[(u0 + (min(q, nitems - 1) / nchunk) * G) / nch].x;
+        const int hpos = hrec.y + min(hr, hrec.z - 1);
+        int hsrc = 0;
+        float hw = 0.0f;
+        if (kG1 && hu < nunits) {
+            hsrc = p.slot_src[hpos];
+            hw = p.slot_w[hpos];
+        }
+
         NarrowBuf<KC> buf[NBUF];
-        // the first items' weights: expert from the sub-tile record directly
 #pragma unroll
         for (int q = 0; q < NBUF - 1; ++q) {
             const int u = u0 + (min(q, nitems - 1) / nchunk) * G;
-            const int m = u / nch;
-            issue_w(buf[q], q, p.sub_rec[m].x, u - m * nch);
+            issue_w(buf[q], q, early_e[q], u % nch);
         }
 
-        // ---- headers of units u0 + j * G, j < kBatch (16 threads per unit)
-        __syncthreads();                                // the previous batch is done with LDS
-        {
-            const int j = tid / kSubRows, r = tid % kSubRows;
-            const int u = u0 + j * G;
-            if (u < nunits) {
-                const int m = u / nch;
-                const int4 rec = p.sub_rec[m];          // {expert, first position, rows}
-                const int pos = rec.y + min(r, rec.z - 1);
-                int arow = pos;
-                float w = 0.0f;
-                if (kG1) {
-                    const int src = p.slot_src[pos];
-                    arow = src / p.topk;
-                    w = p.topk_w[src];
-                }
-                s_arow[j][r] = arow;
-                s_w[j][r] = w;
-                if (r == 0) {
-                    s_hdr[j][0] = rec.x;
-                    s_hdr[j][1] = rec.y;
-                    s_hdr[j][2] = rec.z;
-                    s_hdr[j][3] = u - m * nch;
-                }
+        // ---- headers of units u0 + j * G, j < kBatch, into LDS
+        lds_barrier();                                  // the previous batch is done with LDS
+        if (hu < nunits) {
+            s_arow[hj][hr] = kG1 ? hsrc / p.topk : hpos;
+            s_w[hj][hr] = hw;
+            if (hr == 0) {
+                s_hdr[hj][0] = hrec.x;
+                s_hdr[hj][1] = hrec.y;
+                s_hdr[hj][2] = hrec.z;
+                s_hdr[hj][3] = hu % nch;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         v4f acc[kNT];
         auto epilogue = [&](int j) {

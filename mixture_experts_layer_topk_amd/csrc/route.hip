@@ -65,6 +65,7 @@ __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p)
             int pos = off[e] + s;
             p.slot_src[pos] = (int)i;
             p.slot_of[i] = pos;
+            p.slot_w[pos] = p.wts[i];
         } else {
             p.slot_of[i] = -1;
         }

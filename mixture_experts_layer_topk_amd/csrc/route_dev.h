@@ -65,7 +65,8 @@ MOE_DEV uint32_t wave_min_u32(uint32_t x) { return ~wave_max_u32(~x); }
 // by decreasing logit, smaller index first among equal logits.
 template <int NPL>
 MOE_DEV void route_token(const float (&v)[NPL], int E, int k, int score_fn, int renorm,
-                         int32_t* __restrict__ idx_out, float* __restrict__ w_out, int* lds_idx) {
+                         int32_t* __restrict__ idx_out, float* __restrict__ w_out, int* lds_idx,
+                         float* lds_w) {
     const int lane = threadIdx.x & 63;
     uint32_t ord[NPL];                      // 0: no expert here, or already taken
 #pragma unroll
@@ -119,9 +120,11 @@ MOE_DEV void route_token(const float (&v)[NPL], int E, int k, int score_fn, int 
         denom = wave_sum(z);
     }
     if (lane < k) {
+        const float w = s / denom;
         idx_out[lane] = my_e;
         lds_idx[lane] = my_e;
-        w_out[lane] = s / denom;
+        w_out[lane] = w;
+        if (lds_w) lds_w[lane] = w;
     }
 }
 
@@ -175,7 +178,8 @@ MOE_DEV void quant_rows(const RouteParams& p, int block, int nblocks) {
 // loaded while the current one is routed (more would cost registers that the
 // quantising workgroups of the same kernel need for occupancy).
 template <int NPL, int kThreads>
-MOE_DEV void route_tokens(const RouteParams& p, int64_t t0, int ntok, int* pair_exp) {
+MOE_DEV void route_tokens(const RouteParams& p, int64_t t0, int ntok, int* pair_exp,
+                          float* pair_w) {
     constexpr int W = kThreads / 64;
     constexpr bool kPrefetch = NPL <= 4;
     const int k = p.topk;
@@ -190,7 +194,7 @@ MOE_DEV void route_tokens(const RouteParams& p, int64_t t0, int ntok, int* pair_
         else
             load_logits<NPL>(p.logits + t * p.E, p.E, v);
         route_token<NPL>(v, p.E, k, p.score_fn, p.renorm, p.idx_out + t * k, p.w_out + t * k,
-                         pair_exp + i * k);
+                         pair_exp + i * k, pair_w ? pair_w + i * k : nullptr);
         if (kPrefetch) {
 #pragma unroll
             for (int j = 0; j < NPL; ++j) v[j] = nv[j];
@@ -199,21 +203,24 @@ MOE_DEV void route_tokens(const RouteParams& p, int64_t t0, int ntok, int* pair_
 }
 
 // Route tokens [t0, t0 + ntok) (one wave per token) or take the caller's ids;
-// pair i = (t - t0) * k + j of the chunk gets its expert in pair_exp[i].
+// pair i = (t - t0) * k + j of the chunk gets its expert in pair_exp[i] and, if
+// pair_w is given, its weight in pair_w[i].
 template <int kThreads>
-MOE_DEV void route_chunk(const RouteParams& p, int64_t t0, int ntok, int npl, int* pair_exp) {
+MOE_DEV void route_chunk(const RouteParams& p, int64_t t0, int ntok, int npl, int* pair_exp,
+                         float* pair_w = nullptr) {
     const int tid = threadIdx.x;
     const int k = p.topk;
     if (p.logits) {
-        if (npl <= 1) route_tokens<1, kThreads>(p, t0, ntok, pair_exp);
-        else if (npl <= 2) route_tokens<2, kThreads>(p, t0, ntok, pair_exp);
-        else if (npl <= 4) route_tokens<4, kThreads>(p, t0, ntok, pair_exp);
-        else if (npl <= 8) route_tokens<8, kThreads>(p, t0, ntok, pair_exp);
-        else route_tokens<16, kThreads>(p, t0, ntok, pair_exp);
+        if (npl <= 1) route_tokens<1, kThreads>(p, t0, ntok, pair_exp, pair_w);
+        else if (npl <= 2) route_tokens<2, kThreads>(p, t0, ntok, pair_exp, pair_w);
+        else if (npl <= 4) route_tokens<4, kThreads>(p, t0, ntok, pair_exp, pair_w);
+        else if (npl <= 8) route_tokens<8, kThreads>(p, t0, ntok, pair_exp, pair_w);
+        else route_tokens<16, kThreads>(p, t0, ntok, pair_exp, pair_w);
     } else {
         for (int i = tid; i < ntok * k; i += kThreads) {
             int e = p.idx_in[t0 * k + i];
             pair_exp[i] = e;
+            if (pair_w) pair_w[i] = p.w_in[t0 * k + i];
             if (p.idx_in != p.idx_out) {
                 p.idx_out[t0 * k + i] = e;
                 p.w_out[t0 * k + i] = p.w_in[t0 * k + i];
@@ -349,11 +356,12 @@ MOE_DEV void bucket_small(const RouteParams& rp, const ScatterParams& sp, int np
     __shared__ typename Scan::storage_type tmp;
     __shared__ int pair_exp[kSmallPairs];
     __shared__ int pair_rank[kSmallPairs];
+    __shared__ float pair_w[kSmallPairs];
     const int tid = threadIdx.x;
     const int k = rp.topk, E = rp.E, bm = sp.bm;
     const int npairs = (int)rp.T * k;
     for (int e = tid; e < E; e += kThreads) hist[e] = 0;
-    route_chunk<kThreads>(rp, 0, (int)rp.T, npl, pair_exp);
+    route_chunk<kThreads>(rp, 0, (int)rp.T, npl, pair_exp, pair_w);
     lds_barrier();
     for (int i = tid; i < npairs; i += kThreads) {
         const int e = pair_exp[i];
@@ -407,6 +415,7 @@ MOE_DEV void bucket_small(const RouteParams& rp, const ScatterParams& sp, int np
             const int pos = off[e] + pair_rank[i];
             sp.slot_src[pos] = i;
             sp.slot_of[i] = pos;
+            sp.slot_w[pos] = pair_w[i];
         } else {
             sp.slot_of[i] = -1;
         }
