@@ -64,20 +64,25 @@ def parse():
     return ap.parse_args()
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000      # hipEventDisableSystemFence
+
+
 class Hip:
     """The few HIP runtime calls the timing needs (events on the launch stream)."""
 
     def __init__(self):
         self.lib = ctypes.CDLL("libamdhip64.so")
-        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def event(self):
+        # timing-only events: no system-scope fence (cache write-back and
+        # invalidate) when recorded, which would add several us to each stage
         e = ctypes.c_void_p()
-        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        assert self.lib.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) == 0
         return e
 
     def record(self, e, stream):
