@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--cpu-sample-experts", type=int, default=24,
                     help="experts whose rows the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--gemm-path", choices=("auto", "narrow", "tiled", "one-launch", "one-kernel"),
+    ap.add_argument("--gemm-path", choices=("auto", "narrow", "narrow-one-launch", "tiled", "one-launch",
+                                            "one-kernel"),
                     default="auto", help="GEMM kernels moe_forward uses (default: its own choice)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before the timed steps, copy a buffer of this many MiB once (a "
@@ -182,6 +183,16 @@ def roofline(w, counts, stage_ms, path="auto"):
         return {"kernel": "layer_small_kernel (route + quantise + narrow GEMMs + combine, one launch)",
                 "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "alg_bytes": alg_bytes}
+    if path == "narrow-one-launch":
+        # the narrow GEMM1 and GEMM2 in one kernel: both GEMMs' minimum bytes over its duration
+        touched = int((counts > 0).sum())
+        w2 = w.H * (w.I // 2 + w.I // 32)
+        R = w.T * w.topk
+        alg_bytes = gemm1_algorithmic_bytes(w, counts) + touched * w2 + R * (w.I + w.I // 32 + 2 * w.H)
+        gbs = alg_bytes / (gemm1_ms * 1e-3) / 1e9
+        return {"kernel": "narrow_fused_kernel (narrow GEMM1 + SwiGLU*w + GEMM2, one launch)",
+                "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "alg_bytes": alg_bytes}
     if path == "one-launch":
         # GEMM1 and GEMM2 in one kernel: all the layer's GEMM FLOPs over its duration
         tflops = w.flops() / (gemm1_ms * 1e-3) / 1e12
@@ -277,7 +288,8 @@ def main():
     nstage = m.NUM_STAGE_EVENTS
     ev = [(ctypes.c_void_p * nstage)(*[hip.event() for _ in range(nstage)]) for _ in range(a.steps)]
     flags = {"auto": m.FLAG_NONE, "narrow": m.FLAG_NARROW, "tiled": m.FLAG_TILED,
-             "one-launch": m.FLAG_ONE_LAUNCH, "one-kernel": m.FLAG_ONE_KERNEL}[a.gemm_path]
+             "one-launch": m.FLAG_ONE_LAUNCH, "one-kernel": m.FLAG_ONE_KERNEL,
+             "narrow-one-launch": m.FLAG_NARROW | m.FLAG_ONE_LAUNCH}[a.gemm_path]
     args_plain = m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, flags=flags)
     args_ev = [m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, flags=flags,
                               stage_events=e) for e in ev]

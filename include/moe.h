@@ -88,9 +88,13 @@ typedef struct moe_dims {
  * it needs T * topk <= 1024 (else MOE_EUNSUPPORTED) and implies the narrow
  * GEMMs.  On one MI355X its grid barriers (cache write-backs between XCDs)
  * cost more than the launch boundaries they replace, so it is not the
- * default either.  All paths meet the same tolerance against the definition.  NARROW
- * together with TILED or ONE_LAUNCH is MOE_EINVAL, and so is ONE_KERNEL
- * together with TILED or ONE_LAUNCH. */
+ * default either.  MOE_FLAG_NARROW | MOE_FLAG_ONE_LAUNCH runs the narrow GEMM1
+ * -> SwiGLU -> GEMM2 as one launch whose GEMM2 units wait on per-sub-tile
+ * ready counters; measured slower than the two narrow launches at the decode
+ * shape (GEMM2 cannot start before the slowest GEMM1 unit of its rows), so it
+ * is opt-in.  All paths meet the same tolerance against the definition.
+ * NARROW together with TILED is MOE_EINVAL, and so is ONE_KERNEL together with
+ * TILED or ONE_LAUNCH. */
 #define MOE_FLAG_NONE 0u
 #define MOE_FLAG_NARROW 1u
 #define MOE_FLAG_TILED 2u

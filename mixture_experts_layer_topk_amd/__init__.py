@@ -196,8 +196,8 @@ def forward(d: Dims, x, w13, w13_sf, w2, w2_sf, ws, logits=None, topk_idx=None, 
             y=None, flags=FLAG_NONE):
     """The whole layer; returns y (BF16 [T, H]).  flags: FLAG_NARROW / FLAG_TILED force
     the GEMM kernel family (default: chosen from the rows per expert); FLAG_ONE_LAUNCH
-    runs the tiled GEMMs as one launch with ready counters; FLAG_ONE_KERNEL runs the whole
-    layer as one launch (T * topk <= 1024)."""
+    runs the tiled GEMMs (or, with FLAG_NARROW, the narrow ones) as one launch with ready
+    counters; FLAG_ONE_KERNEL runs the whole layer as one launch (T * topk <= 1024)."""
     if y is None:
         y = torch.empty((d.T, d.H), dtype=torch.bfloat16, device=x.device)
     forward_raw(forward_args(d, x, w13, w13_sf, w2, w2_sf, y, ws, logits, topk_idx, topk_w,

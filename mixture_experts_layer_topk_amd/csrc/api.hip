@@ -56,7 +56,7 @@ Carve carve(const moe_dims_t& d) {
     c.mtile_rec = take((max_mtiles(d) + 1) * 16);
     c.sub_rec = take((max_subs(d) + 1) * 16);
     c.nsub = take(4);
-    c.ready = take(max_mtiles(d) * 4);
+    c.ready = take(std::max(max_mtiles(d), max_subs(d)) * 4);
     c.topk_idx = take(R * 4);
     c.topk_w = take(R * 4);
     c.slot_in_e = take(R * 4);
@@ -184,6 +184,7 @@ int moe_route(const moe_dims_t* d, const float* logits, int32_t* topk_idx, float
     sp.sub_rec = at<int4>(ws, c.sub_rec);
     sp.nsub = at<int32_t>(ws, c.nsub);
     sp.max_subs = (int)max_subs(*d);
+    sp.nready = (int)std::max(max_mtiles(*d), max_subs(*d));
     sp.ready = at<int>(ws, c.ready);
     sp.status = at<int>(ws, c.status);
     hipError_t err = moe::launch_route(rp, sp, s);
@@ -227,7 +228,7 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     if (!a->logits && (!a->topk_idx || !a->topk_w)) return MOE_EINVAL;
     const uint32_t f = a->flags;
     if ((f & ~(MOE_FLAG_NARROW | MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH | MOE_FLAG_ONE_KERNEL)) ||
-        ((f & MOE_FLAG_NARROW) && (f & (MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH))) ||
+        ((f & MOE_FLAG_NARROW) && (f & MOE_FLAG_TILED)) ||
         ((f & MOE_FLAG_ONE_KERNEL) && (f & (MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH))))
         return MOE_EINVAL;
     if ((f & MOE_FLAG_ONE_KERNEL) && !moe::layer_small_fits(d.T, d.topk)) return MOE_EUNSUPPORTED;
@@ -277,6 +278,7 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     sp.sub_rec = at<int4>(ws, c.sub_rec);
     sp.nsub = at<int32_t>(ws, c.nsub);
     sp.max_subs = (int)max_subs(d);
+    sp.nready = (int)std::max(max_mtiles(d), max_subs(d));
     sp.ready = at<int>(ws, c.ready);
     sp.status = at<int>(ws, c.status);
     hipEvent_t* ev = a->stage_events;
@@ -328,12 +330,14 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     // few rows per expert on average: the weight-streaming (narrow) kernels
     bool narrow = R <= kNarrowRowsPerExpert * (int64_t)d.E;
     if (a->flags & MOE_FLAG_NARROW) narrow = true;
-    if (a->flags & (MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH)) narrow = false;
+    if (a->flags & MOE_FLAG_TILED) narrow = false;
+    // ONE_LAUNCH alone keeps its tiled meaning; with NARROW it fuses the narrow GEMMs
+    if ((a->flags & MOE_FLAG_ONE_LAUNCH) && !(a->flags & MOE_FLAG_NARROW)) narrow = false;
     const bool fused = (a->flags & MOE_FLAG_ONE_LAUNCH) != 0;
     if (ev) err = hipEventRecord(ev[1], s);
     if (fused) {
         // GEMM1 -> SwiGLU -> GEMM2 in one launch: both events after it
-        if (err == hipSuccess) err = moe::launch_fused_gemm(gp, s);
+        if (err == hipSuccess) err = narrow ? moe::launch_narrow_fused(gp, s) : moe::launch_fused_gemm(gp, s);
         if (err == hipSuccess && ev) err = hipEventRecord(ev[2], s);
     } else {
         if (err == hipSuccess) err = narrow ? moe::launch_narrow_gemm1(gp, s) : moe::launch_gemm1(gp, s);

@@ -40,7 +40,7 @@ struct ScatterParams {
                                 // past the last m-tile
     int4* sub_rec;              // [max_subs] the same for 16-row sub-tiles
     int32_t* nsub;              // [1] number of 16-row sub-tiles
-    int* ready;                 // [max_mtiles] zeroed here for the one-launch GEMMs
+    int* ready;                 // [nready] zeroed here for the one-launch GEMMs
     int* status;                // [1] zeroed here
     int32_t* slot_src;          // [T*k]
     int32_t* slot_of;           // [T, k]
@@ -48,6 +48,7 @@ struct ScatterParams {
     float* slot_w;              // [T*k] routing weight of the pair at each position
     int64_t T;
     int E, topk, bm, max_mtiles, max_subs;
+    int nready;                 // max(max_mtiles, max_subs)
 };
 
 hipError_t launch_route(const RouteParams& rp, const ScatterParams& sp, hipStream_t s);
@@ -85,7 +86,9 @@ struct GemmParams {
     int max_mtiles;             // upper bound of mtile_off[E]
     int max_subs;               // upper bound of *nsub
     // one-launch GEMM1 -> GEMM2 (both zeroed by the bucketing stage of the call)
-    int* ready;                 // [max_mtiles] GEMM1 n-tiles of the m-tile whose h is stored
+    int* ready;                 // [max(max_mtiles, max_subs)] GEMM1 n-tiles of the m-tile (tiled
+                                // one-launch) or GEMM1 units of the sub-tile (narrow one-launch)
+                                // whose h is stored
     int* status;                // [1] set to 1 if a wait gave up (never in a correct run)
     int wave_experts;           // experts per scheduling wave (set by the launcher)
 };
@@ -99,6 +102,7 @@ hipError_t launch_fused_gemm(const GemmParams& p, hipStream_t s);
 // workgroups that stream weights straight into registers
 hipError_t launch_narrow_gemm1(const GemmParams& p, hipStream_t s);
 hipError_t launch_narrow_gemm2(const GemmParams& p, hipStream_t s);
+hipError_t launch_narrow_fused(const GemmParams& p, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* o, const int32_t* slot_of, int64_t T, int topk, int H,
                           uint16_t* y, hipStream_t s);

@@ -51,4 +51,41 @@ static hipError_t launch_narrow(const GemmParams& p, hipStream_t s) {
 hipError_t launch_narrow_gemm1(const GemmParams& p, hipStream_t s) { return launch_narrow<true>(p, s); }
 hipError_t launch_narrow_gemm2(const GemmParams& p, hipStream_t s) { return launch_narrow<false>(p, s); }
 
+// GEMM1 -> SwiGLU -> GEMM2 of the narrow kernels in one launch: every
+// workgroup runs its GEMM1 units, then its GEMM2 units, whose activation loads
+// wait on per-sub-tile ready counters (zeroed by the bucketing stage of the
+// call) while their first weight loads are already in flight.  The waits end:
+// no workgroup waits before it has finished its own GEMM1 units, and the grid
+// is capped at the number of workgroups the GPU holds at once.  A wait longer
+// than kNarrowSpinLimit polls sets *p.status and gives up (wrong output, never
+// a hang).
+__global__ __launch_bounds__(kNarrowThreads) void narrow_fused_kernel(GemmParams p) {
+    narrow_gemm<true, true>(p, blockIdx.x, gridDim.x);
+    narrow_gemm<false, true>(p, blockIdx.x, gridDim.x);
+}
+
+hipError_t launch_narrow_fused(const GemmParams& p, hipStream_t s) {
+    static int cus = 0, per_cu = 0;
+    if (cus == 0) {
+        int dev = 0, occ = 0;
+        hipError_t err = hipGetDevice(&dev);
+        if (err == hipSuccess)
+            err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err == hipSuccess)
+            err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, narrow_fused_kernel, kNarrowThreads, 0);
+        if (err != hipSuccess) {
+            cus = 0;
+            return err;
+        }
+        per_cu = std::min(occ, kNarrowBlocksPerCU);
+    }
+    if (per_cu < 1) return hipErrorInvalidConfiguration;
+    const int nch = std::max(p.I / NarrowCfg<true>::kCols, p.H / NarrowCfg<false>::kCols);
+    const int64_t units = (int64_t)p.max_subs * nch;
+    const int64_t grid = std::min<int64_t>(units, (int64_t)per_cu * cus);
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL(narrow_fused_kernel, dim3((unsigned)grid), dim3(kNarrowThreads), 0, s, p);
+    return hipGetLastError();
+}
+
 }  // namespace moe

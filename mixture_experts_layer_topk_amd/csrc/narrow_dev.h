@@ -13,6 +13,7 @@ constexpr int kNarrowThreads = 64 * kNarrowWaves;
 constexpr int kNT = 4;                  // 16-column MFMA tiles per unit
 constexpr int kBatch = kNarrowThreads / kSubRows;   // unit headers fetched per batch
 constexpr int kNarrowBlocksPerCU = 2;
+constexpr int kNarrowSpinLimit = 1 << 14;   // polls of a ready counter before giving up (~20 ms)
 
 template <bool kG1>
 struct NarrowCfg {
@@ -35,7 +36,14 @@ struct NarrowBuf {
 
 // The GEMM of workgroup `bid` of `G` (any G >= 1: the units are dealt out
 // persistently).
-template <bool kG1>
+//
+// kCoh: GEMM1 and GEMM2 run in one launch (the GEMM1 part, then the GEMM2
+// part, in every workgroup).  The XCDs' L2 caches are not coherent within a
+// launch, so GEMM1 stores h with device-coherent stores, waits for them to
+// complete and then adds each finished unit to ready[sub-tile]; a GEMM2 batch
+// issues its first weight loads, waits until ready[] counts every GEMM1 unit
+// of each of its sub-tiles and then reads h with device-coherent loads.
+template <bool kG1, bool kCoh = false>
 MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
     using Cfg = NarrowCfg<kG1>;
     constexpr int KC = Cfg::KC, NBUF = Cfg::NBUF;
@@ -112,9 +120,21 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
 #pragma unroll
             for (int jj = 0; jj < KC; ++jj) {
                 const int ks = max(0, min(kb + c * KC + jj, min(ke, nk) - 1));
-                bf.alo[jj] = *reinterpret_cast<const v4i*>(ap + ks * kKStep);
-                bf.ahi[jj] = *reinterpret_cast<const v4i*>(ap + ks * kKStep + 64);
-                bf.sa[jj] = *reinterpret_cast<const uint32_t*>(asp + ks * a_slab);
+                if constexpr (kCoh && !kG1) {
+                    // h of this launch: device-coherent dword loads
+                    auto ld = [](const uint8_t* q) {
+                        return (int)__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(q)),
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    };
+                    const uint8_t* a0 = ap + ks * kKStep;
+                    bf.alo[jj] = v4i{ld(a0), ld(a0 + 4), ld(a0 + 8), ld(a0 + 12)};
+                    bf.ahi[jj] = v4i{ld(a0 + 64), ld(a0 + 68), ld(a0 + 72), ld(a0 + 76)};
+                    bf.sa[jj] = (uint32_t)ld(asp + ks * a_slab);
+                } else {
+                    bf.alo[jj] = *reinterpret_cast<const v4i*>(ap + ks * kKStep);
+                    bf.ahi[jj] = *reinterpret_cast<const v4i*>(ap + ks * kKStep + 64);
+                    bf.sa[jj] = *reinterpret_cast<const uint32_t*>(asp + ks * a_slab);
+                }
             }
         };
         auto issue = [&](NarrowBuf<KC>& bf, int q) {
@@ -163,6 +183,24 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
             }
         }
         lds_barrier();
+        if constexpr (kCoh && !kG1) {
+            // every GEMM1 unit of this batch's sub-tiles has stored its h columns
+            if (tid == 0) {
+                const int need = p.I / NarrowCfg<true>::kCols;
+                for (int j = 0; j < nb; ++j) {
+                    const int m = (u0 + j * G) / nch;
+                    int n = 0;
+                    while (__hip_atomic_load(p.ready + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+                        __builtin_amdgcn_s_sleep(1);
+                        if (++n > kNarrowSpinLimit) {
+                            __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            break;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
 
         v4f acc[kNT];
         auto epilogue = [&](int j) {
@@ -202,10 +240,20 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
                             e4m3_block_exp(fmaxf(s_amax[0][4 * lg + i], s_amax[1][4 * lg + i]));
                         if (r < valid) {
                             const int64_t pos = p0 + r;
-                            p.hq[pos * p.I + icol] = (uint8_t)e4m3_pack2(h[i] * exp2_neg(ex), 0.0f);
-                            if (wave == 0 && l16 == 0)
-                                p.hsf[(int64_t)(icol / (4 * kGroup)) * (R * 4) + pos * 4 +
-                                      (icol / kGroup) % 4] = (uint8_t)(ex + 127);
+                            uint8_t* hq = p.hq + pos * p.I + icol;
+                            const uint8_t code = (uint8_t)e4m3_pack2(h[i] * exp2_neg(ex), 0.0f);
+                            uint8_t* hsf = p.hsf + (int64_t)(icol / (4 * kGroup)) * (R * 4) + pos * 4 +
+                                           (icol / kGroup) % 4;
+                            const bool sf = wave == 0 && l16 == 0;
+                            if constexpr (kCoh) {
+                                __hip_atomic_store(hq, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                if (sf)
+                                    __hip_atomic_store(hsf, (uint8_t)(ex + 127), __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+                            } else {
+                                *hq = code;
+                                if (sf) *hsf = (uint8_t)(ex + 127);
+                            }
                         }
                     }
                 }
@@ -250,6 +298,13 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
                 issue(buf[(b + NBUF - 1) % NBUF], q0 + b + NBUF - 1);
                 if (q0 + b < nitems) consume(buf[b], q0 + b);
             }
+        }
+        if constexpr (kCoh && kG1) {
+            // this batch's h stores have completed (vmcnt(0)); count its units in
+            __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8) | (0 << 14));
+            __syncthreads();
+            if (hr == 0 && hu < nunits)
+                __hip_atomic_fetch_add(p.ready + hu / nch, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

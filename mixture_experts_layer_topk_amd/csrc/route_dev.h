@@ -301,7 +301,7 @@ MOE_DEV void write_tables(const ScatterParams& p, const int* cnt, const int* off
         for (int e = tid; e < p.E; e += kRouteThreads) p.counts_out[e] = cnt[e];
         for (int e = tid; e <= p.E; e += kRouteThreads) p.offsets_out[e] = off[e];
         // the one-launch GEMMs' per-m-tile counters and status start at zero
-        for (int m = tid; m < p.max_mtiles; m += kRouteThreads) p.ready[m] = 0;
+        for (int m = tid; m < p.nready; m += kRouteThreads) p.ready[m] = 0;
         if (tid == 0) *p.status = 0;
     }
     for (int pass = 0; pass < 2; ++pass) {
@@ -407,7 +407,7 @@ MOE_DEV void bucket_small(const RouteParams& rp, const ScatterParams& sp, int np
     const int4 zero = make_int4(0, 0, 0, 0);
     for (int m = n_mtiles + tid; m < sp.max_mtiles; m += kThreads) sp.mtile_rec[m] = zero;
     for (int m = n_subs + tid; m < sp.max_subs; m += kThreads) sp.sub_rec[m] = zero;
-    for (int m = tid; m < sp.max_mtiles; m += kThreads) sp.ready[m] = 0;
+    for (int m = tid; m < sp.nready; m += kThreads) sp.ready[m] = 0;
     lds_barrier();                                        // off[] complete
     for (int i = tid; i < npairs; i += kThreads) {
         const int e = pair_exp[i];

@@ -236,8 +236,8 @@ AGREE_SHAPES = [W.WORKLOADS["decode"], W.WORKLOADS["tiny"], RAGGED,
 
 @pytest.mark.parametrize("w", AGREE_SHAPES, ids=lambda w: w.name)
 def test_narrow_and_tiled_gemms_match_oracle(w):
-    """Every GEMM path (narrow; tiled in one launch; tiled in two launches), forced on
-    the same inputs, against the oracle (the default picks one per shape)."""
+    """Every GEMM path (narrow in two launches or one; tiled in one launch or two),
+    forced on the same inputs, against the oracle (the default picks one per shape)."""
     m = G.lib()
     _log(f"narrow and tiled {w.name}")
     ext = None
@@ -246,8 +246,8 @@ def test_narrow_and_tiled_gemms_match_oracle(w):
     dl = G.DeviceLayer(w, external_topk=ext)
     ref = _oracle_full(w, ext)
     so_r = ref["slot_of"].reshape(-1)
-    paths = [("narrow", m.FLAG_NARROW), ("tiled, two launches", m.FLAG_TILED),
-             ("tiled, one launch", m.FLAG_ONE_LAUNCH)]
+    paths = [("narrow", m.FLAG_NARROW), ("narrow, one launch", m.FLAG_NARROW | m.FLAG_ONE_LAUNCH),
+             ("tiled, two launches", m.FLAG_TILED), ("tiled, one launch", m.FLAG_ONE_LAUNCH)]
     if w.T * w.topk <= 1024:
         paths.append(("whole layer, one kernel", m.FLAG_ONE_KERNEL))
     for name, flag in paths:
@@ -302,6 +302,29 @@ def test_one_launch_reads_this_calls_h():
     for dl, ref in ((da, ra), (db, rb), (da, ra), (db, rb)):
         y = dl.forward(flags=m.FLAG_ONE_LAUNCH)
         G.check_y(G.y_bits(y), ref["y"])
+
+
+def test_narrow_one_launch_reads_this_calls_h():
+    """The narrow GEMMs in one launch on alternating inputs and shapes sharing one
+    workspace: a GEMM2 unit that read h left in a cache by the previous call, or
+    started before this call's GEMM1 units of its sub-tile had stored theirs, would
+    give the other input's result."""
+    m = G.lib()
+    wa = W.WORKLOADS["decode"]
+    wb = W.Workload("decode_b", T=8, H=2048, I=512, E=256, topk=8, seed=1)
+    wc = W.Workload("mid_b", T=96, H=2048, I=512, E=32, topk=8, seed=2)
+    _log("narrow one launch, alternating inputs")
+    da, db, dc = G.DeviceLayer(wa), G.DeviceLayer(wb), G.DeviceLayer(wc)
+    db.ws = da.ws
+    if dc.ws.numel() > da.ws.numel():
+        da.ws = db.ws = dc.ws
+    else:
+        dc.ws = da.ws
+    refs = [_oracle_full(w) for w in (wa, wb, wc)]
+    for _ in range(2):
+        for dl, ref in zip((da, db, dc), refs):
+            y = dl.forward(flags=m.FLAG_NARROW | m.FLAG_ONE_LAUNCH)
+            G.check_y(G.y_bits(y), ref["y"])
 
 
 def test_one_kernel_layer_reads_this_calls_data():

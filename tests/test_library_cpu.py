@@ -71,7 +71,7 @@ def test_forward_rejects_null_and_small_workspace_without_gpu():
     a.ws = ctypes.c_void_p(1 << 20)
     assert m._lib.moe_forward(ctypes.byref(a), None) == m.MOE_EINVAL
     a.x = fake
-    for bad_flags in (m.FLAG_NARROW | m.FLAG_TILED, m.FLAG_NARROW | m.FLAG_ONE_LAUNCH,
+    for bad_flags in (m.FLAG_NARROW | m.FLAG_TILED, m.FLAG_NARROW | m.FLAG_TILED | m.FLAG_ONE_LAUNCH,
                       m.FLAG_ONE_KERNEL | m.FLAG_TILED, m.FLAG_ONE_KERNEL | m.FLAG_ONE_LAUNCH,
                       16, 1 << 31):                                            # unknown or conflicting
         a.flags = bad_flags
