@@ -162,9 +162,10 @@ def test_forward_decode_matches_oracle():
     G.check_y(G.y_bits(y), ref["y"])
 
 
-@pytest.mark.parametrize("name", ["dsv3_prefill", "dsv3_skewed"])
+@pytest.mark.parametrize("name", ["dsv3_prefill", "dsv3_skewed", "full256"])
 def test_forward_full_size_sampled_tokens(name):
-    """Full-size launch; the oracle recomputes a sample of tokens one by one."""
+    """Full-size launch; the oracle recomputes a sample of tokens one by one (only
+    the experts those tokens touch are generated and quantised on its side)."""
     w = W.WORKLOADS[name]
     _log(f"forward {name} (sampled)")
     dl = G.DeviceLayer(w)
@@ -176,7 +177,7 @@ def test_forward_full_size_sampled_tokens(name):
     G.check_bucketize(inter, idx, w.E)
     toks = [0, w.T // 3, 2 * w.T // 3, w.T - 1]
     ref = M.forward(dl.x_np, *G.oracle_weights(w), topk=w.topk, I=w.I, logits=logits,
-                    tokens=toks)
+                    score_fn=w.score_fn, renorm=bool(w.renorm), tokens=toks)
     G.check_y(G.y_bits(y), ref["y"], rows=toks)
     so_g = inter["slot_of"][toks].reshape(-1)
     so_r = ref["slot_of"][toks].reshape(-1)
