@@ -40,6 +40,17 @@ __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p)
     __shared__ BlockScan::storage_type tmp;
     __shared__ int last;
     const int tid = threadIdx.x;
+    // this thread's first pair, loaded before the counters so that the two
+    // round trips overlap (they do not depend on each other)
+    const int64_t npairs = p.T * p.topk;
+    const int64_t i0 = (int64_t)blockIdx.x * kRouteThreads + tid;
+    int e0 = -1, s0 = -1;
+    float w0 = 0.0f;
+    if (i0 < npairs) {
+        e0 = p.idx[i0];
+        s0 = p.slot_in_e[i0];
+        w0 = p.wts[i0];
+    }
     for (int e = tid; e < p.E; e += kRouteThreads)
         cnt[e] = __hip_atomic_load(&p.cnt[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
@@ -56,16 +67,14 @@ __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p)
         if (tid == 0) *p.arrive = 0;
     }
     write_tables(p, cnt, off, tiles, toff, tmp, blockIdx.x, gridDim.x);
-    const int64_t npairs = p.T * p.topk;
-    for (int64_t i = (int64_t)blockIdx.x * kRouteThreads + tid; i < npairs;
-         i += (int64_t)gridDim.x * kRouteThreads) {
-        int e = p.idx[i];
-        int s = p.slot_in_e[i];
+    for (int64_t i = i0; i < npairs; i += (int64_t)gridDim.x * kRouteThreads) {
+        const int e = i == i0 ? e0 : p.idx[i];
+        const int s = i == i0 ? s0 : p.slot_in_e[i];
         if (e >= 0 && e < p.E && s >= 0) {
             int pos = off[e] + s;
             p.slot_src[pos] = (int)i;
             p.slot_of[i] = pos;
-            p.slot_w[pos] = p.wts[i];
+            p.slot_w[pos] = i == i0 ? w0 : p.wts[i];
         } else {
             p.slot_of[i] = -1;
         }
