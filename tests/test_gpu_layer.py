@@ -23,7 +23,9 @@ RAGGED = W.Workload("ragged", T=601, H=640, I=384, E=5, topk=2)
 SMALL_SHAPES = [W.WORKLOADS["tiny"], RAGGED,
                 W.Workload("k1", T=77, H=256, I=128, E=3, topk=1),
                 W.Workload("sig", T=130, H=384, I=256, E=16, topk=4, score_fn=W.SIGMOID),
-                W.Workload("t1", T=1, H=128, I=128, E=4, topk=2)]
+                W.Workload("t1", T=1, H=128, I=128, E=4, topk=2),
+                # raw sigmoid weights (no renormalisation) reach the GEMM1 epilogue
+                W.Workload("sig_raw", T=70, H=256, I=128, E=12, topk=3, score_fn=W.SIGMOID, renorm=0)]
 
 
 def _log(msg):
@@ -86,7 +88,15 @@ def test_pack_weights_bit_exact(rows, cols):
 # multi-workgroup path with global counters
 ROUTE_EDGES = {"pairs1024": W.Workload("pairs1024", T=128, H=256, I=128, E=32, topk=8),
                "pairs1032": W.Workload("pairs1032", T=129, H=256, I=128, E=32, topk=8),
-               "e1024": W.Workload("e1024", T=3, H=128, I=128, E=1024, topk=16, score_fn=W.SIGMOID)}
+               "e1024": W.Workload("e1024", T=3, H=128, I=128, E=1024, topk=16, score_fn=W.SIGMOID),
+               # weights without renormalisation: the full softmax over E, or the raw sigmoid
+               "softmax_full": W.Workload("softmax_full", T=50, H=128, I=128, E=100, topk=6, renorm=0),
+               "sigmoid_raw": W.Workload("sigmoid_raw", T=40, H=128, I=128, E=200, topk=8,
+                                         score_fn=W.SIGMOID, renorm=0),
+               # every expert chosen by every token; many tokens on the multi-workgroup path
+               "k_eq_e": W.Workload("k_eq_e", T=20, H=128, I=128, E=8, topk=8),
+               "softmax_full_big": W.Workload("softmax_full_big", T=300, H=128, I=128, E=48, topk=4,
+                                              renorm=0)}
 
 
 @pytest.mark.parametrize("name", list(W.WORKLOADS) + list(ROUTE_EDGES))
