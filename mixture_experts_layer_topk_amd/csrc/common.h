@@ -104,6 +104,16 @@ MOE_DEV void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Largest x over each row of 16 lanes of a fully active wave, in every lane of
+// the row: DPP butterflies (lane pairs 1 apart, 2 apart, then the mirrored
+// halves of 8 and of 16).
+MOE_DEV uint32_t row_max_u32(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));
+    return max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));
+}
+
 // Wave-level reductions over 64 lanes.
 MOE_DEV float wave_max(float v) {
 #pragma unroll

@@ -223,10 +223,10 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         h[i] = swiglu_w(g[i], u[i], s_w[j][4 * lg + i]);
-                        float m = __builtin_fabsf(h[i]);
-#pragma unroll
-                        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-                        if (l16 == 0) s_amax[wave][4 * lg + i] = m;
+                        // max |h| over the row's 16 columns (bit patterns of
+                        // non-negative floats order like the values)
+                        const uint32_t m = row_max_u32(f2u(h[i]) & 0x7FFFFFFFu);
+                        if (l16 == 0) s_amax[wave][4 * lg + i] = u2f(m);
                     }
                 }
                 // an E4M3 group is the unit's 32 I columns: both waves' maxima

@@ -34,15 +34,8 @@ MOE_DEV void load_logits(const float* __restrict__ lrow, int E, float (&v)[NPL])
 }
 
 // Largest (smallest) of x over the 64 lanes of a fully active wave, in every
-// lane: butterflies inside each row of 16 lanes by DPP (lane pairs 1 apart, 2
-// apart, then the mirrored halves of 8 and of 16), then the four row results
+// lane: row_max_u32 inside each row of 16 lanes, then the four row results
 // through scalar registers.
-MOE_DEV uint32_t row_max_u32(uint32_t x) {
-    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));
-    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));
-    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));
-    return max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));
-}
 MOE_DEV uint32_t wave_max_u32(uint32_t x) {
     x = row_max_u32(x);
     const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)x, 0),
