@@ -47,11 +47,13 @@ template <bool kG1, bool kCoh = false>
 MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
     using Cfg = NarrowCfg<kG1>;
     constexpr int KC = Cfg::KC, NBUF = Cfg::NBUF;
-    __shared__ v4f s_red[kNarrowWaves][kNT][64];       // partial accumulators
+    // partial accumulators, two buffers: unit j writes buffer j % 2, whose
+    // previous readers (unit j - 2) finished before unit j - 1's barrier
+    __shared__ v4f s_red2[2][kNarrowWaves][kNT][64];
     __shared__ int s_hdr[kBatch][4];                   // expert, first position, rows, chunk
     __shared__ int s_arow[kBatch][kSubRows];           // activation row of each unit row
-    __shared__ float s_w[kBatch][kSubRows];            // routing weight (GEMM1)
-    __shared__ float s_amax[2][16];
+    __shared__ __attribute__((aligned(16))) float s_w[kBatch][kSubRows];   // routing weight (GEMM1)
+    __shared__ __attribute__((aligned(16))) float s_amax[2][16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -205,7 +207,7 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
         v4f acc[kNT];
         auto epilogue = [&](int j) {
             const int p0 = s_hdr[j][1], valid = s_hdr[j][2], nc = s_hdr[j][3];
-            __syncthreads();                            // s_red of the previous unit is read
+            v4f (&s_red)[kNarrowWaves][kNT][64] = s_red2[j & 1];
 #pragma unroll
             for (int t = 0; t < kNT; ++t) s_red[wave][t][lane] = acc[t];
             __syncthreads();
@@ -220,9 +222,10 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
                         g += s_red[w][wave][lane];
                         u += s_red[w][2 + wave][lane];
                     }
+                    const v4f wr = *reinterpret_cast<const v4f*>(&s_w[j][4 * lg]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        h[i] = swiglu_w(g[i], u[i], s_w[j][4 * lg + i]);
+                        h[i] = swiglu_w(g[i], u[i], wr[i]);
                         // max |h| over the row's 16 columns (bit patterns of
                         // non-negative floats order like the values)
                         const uint32_t m = row_max_u32(f2u(h[i]) & 0x7FFFFFFFu);
@@ -233,11 +236,12 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
                 __syncthreads();
                 if (wave < 2) {
                     const int icol = nc * Cfg::kCols + wave * 16 + l16;
+                    const v4f m0 = *reinterpret_cast<const v4f*>(&s_amax[0][4 * lg]);
+                    const v4f m1 = *reinterpret_cast<const v4f*>(&s_amax[1][4 * lg]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = 4 * lg + i;
-                        const int ex =
-                            e4m3_block_exp(fmaxf(s_amax[0][4 * lg + i], s_amax[1][4 * lg + i]));
+                        const int ex = e4m3_block_exp(fmaxf(m0[i], m1[i]));
                         if (r < valid) {
                             const int64_t pos = p0 + r;
                             uint8_t* hq = p.hq + pos * p.I + icol;
