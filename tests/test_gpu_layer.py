@@ -196,6 +196,23 @@ def test_forward_full_size_sampled_tokens(name):
     assert torch.isfinite(y.float()).all()
 
 
+@pytest.mark.parametrize("path", ["narrow", "tiled"])
+def test_token_permutation_permutes_y_bit_exactly(path):
+    """Each output row depends only on its own token, and each accumulation runs in a
+    fixed order whatever a row's position inside its expert segment, so permuting the
+    tokens permutes y bit for bit (the oracle's own permutation pin, on the GPU)."""
+    m = G.lib()
+    _log(f"token permutation ({path})")
+    flags = m.FLAG_NARROW if path == "narrow" else m.FLAG_TILED
+    dl = G.DeviceLayer(RAGGED)
+    y = dl.forward(flags=flags).clone()
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(RAGGED.T)).to(y.device)
+    dl.x = dl.x[perm].contiguous()
+    dl.logits = dl.logits[perm].contiguous()
+    y_perm = dl.forward(flags=flags)
+    assert torch.equal(y_perm.view(torch.int16), y[perm].view(torch.int16))
+
+
 def test_forward_external_topk_with_masked_slots():
     w = W.Workload("ext", T=257, H=256, I=256, E=6, topk=3)
     _log("forward external topk")
