@@ -37,7 +37,7 @@ PEAK_HBM_GBS = 8000.0
 # workloads whose GEMMs stream more weight bytes than they have FLOPs to hide
 HBM_BOUND = {"decode"}
 KERNEL_SOURCES = ("gemm.hip", "narrow.hip", "narrow_dev.h", "mfma.h", "common.h", "kernels.h")
-NARROW_ROWS_PER_EXPERT = 16        # moe_forward's choice between the two GEMM kernel families
+NARROW_ROWS_PER_EXPERT = 3         # moe_forward's choice between the two GEMM kernel families
 
 
 def parse():
@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="run the workload's shapes with this many tokens instead (sweeps)")
     ap.add_argument("--cpu-sample-experts", type=int, default=24,
                     help="experts whose rows the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -276,6 +278,9 @@ def main():
     import mixture_experts_layer_topk_amd as m
 
     w = W.WORKLOADS[a.workload]
+    if a.tokens is not None:
+        from dataclasses import replace
+        w = replace(w.with_tokens(a.tokens), name=f"{w.name}_T{a.tokens}")
     if a.flush_mb is None:
         a.flush_mb = 1024 if w.name in HBM_BOUND else 0
     x, logits, w13q, w13sf, w2q, w2sf = setup_device(w, m, torch)

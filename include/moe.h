@@ -76,7 +76,7 @@ typedef struct moe_dims {
  * output tiles staged through LDS, for many rows per expert) or as narrow
  * kernels (weights streamed from HBM straight into registers over many small
  * workgroups, for few rows per expert, the decode regime).  By default
- * moe_forward takes the narrow kernels when T * topk <= 16 * E, else the tiled
+ * moe_forward takes the narrow kernels when T * topk <= 3 * E, else the tiled
  * GEMM1 and GEMM2 as two launches ordered by the stream.  MOE_FLAG_ONE_LAUNCH
  * runs the tiled GEMM1 -> SwiGLU -> GEMM2 as one persistent launch whose GEMM2
  * tiles wait on per-m-tile ready counters, experts grouped in waves ("MegaMoE"

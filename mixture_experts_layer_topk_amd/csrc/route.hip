@@ -81,8 +81,9 @@ __global__ __launch_bounds__(kRouteThreads) void scatter_kernel(ScatterParams p)
     }
 }
 
-// Few pairs (T * k <= kSmallPairs): workgroup 0 routes and buckets every pair
-// with no second launch; the other workgroups quantise x meanwhile.
+// Few tokens (T <= kSmallTokens, T * k <= kSmallPairs): workgroup 0 routes and
+// buckets every pair with no second launch; the other workgroups quantise x
+// meanwhile.
 __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(RouteParams rp, ScatterParams sp,
                                                                     int npl) {
     if (blockIdx.x == 0) {
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(RouteParams 
 }
 
 hipError_t launch_route(const RouteParams& rp, const ScatterParams& sp, hipStream_t s) {
-    if (rp.T > 0 && rp.T * rp.topk <= kSmallPairs) {
+    if (rp.T > 0 && rp.T <= kSmallTokens && rp.T * rp.topk <= kSmallPairs) {
         // workgroup 0 routes and buckets; the others quantise x
         int64_t quant_blocks = rp.x ? (rp.T * (rp.H / 8) + kSmallThreads - 1) / kSmallThreads : 0;
         dim3 grid((unsigned)(1 + std::min<int64_t>(quant_blocks, 2048)));

@@ -84,9 +84,11 @@ def test_pack_weights_bit_exact(rows, cols):
 
 # ------------------------------------------------------------------ routing
 
-# T * k = 1024 pairs is the largest case one workgroup buckets on its own; 1032 takes the
-# multi-workgroup path with global counters
-ROUTE_EDGES = {"pairs1024": W.Workload("pairs1024", T=128, H=256, I=128, E=32, topk=8),
+# 32 tokens is the most the one-workgroup routing launch takes; 33 take the
+# multi-workgroup path with global counters (as do 128 and 129, with 1024 and 1032 pairs)
+ROUTE_EDGES = {"tokens32": W.Workload("tokens32", T=32, H=256, I=128, E=300, topk=16),
+               "tokens33": W.Workload("tokens33", T=33, H=256, I=128, E=300, topk=16),
+               "pairs1024": W.Workload("pairs1024", T=128, H=256, I=128, E=32, topk=8),
                "pairs1032": W.Workload("pairs1032", T=129, H=256, I=128, E=32, topk=8),
                "e1024": W.Workload("e1024", T=3, H=128, I=128, E=1024, topk=16, score_fn=W.SIGMOID),
                # weights without renormalisation: the full softmax over E, or the raw sigmoid
