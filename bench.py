@@ -43,8 +43,8 @@ NARROW_ROWS_PER_EXPERT = 3         # moe_forward's choice between the two GEMM k
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--tokens", type=int, default=None,
                     help="run the workload's shapes with this many tokens instead (sweeps)")
@@ -342,6 +342,8 @@ def main():
         for s in range(nstage - 1):
             stage_ms[s] += hip.elapsed_ms(e[s], e[s + 1])
     stage_ms /= a.steps
+    # spread of the step time over the stage pass (its events add a few us per step)
+    step_ms = np.array([hip.elapsed_ms(e[0], e[nstage - 1]) for e in ev])
     tokens_s = w.T / (ms * 1e-3)
 
     counts = m.intermediates(d, ws)["counts"].cpu().numpy()
@@ -365,6 +367,8 @@ def main():
         "layer_tflops": round(layer_tflops, 2),
         "layer_frac_mfma": round(layer_tflops / PEAK_MFMA_FP8_TFLOPS, 4),
         "stages_ms": {n: round(float(v), 4) for n, v in zip(m.STAGES, stage_ms)},
+        "stage_pass_step_ms": {q: round(float(np.percentile(step_ms, pq)), 4)
+                               for q, pq in (("p10", 10), ("p50", 50), ("p90", 90))},
         "roofline": roofline(w, counts, stage_ms, a.gemm_path),
     }
     if not a.no_cpu_baseline:
