@@ -175,8 +175,18 @@ def layer_algorithmic_bytes(w, counts) -> float:
     return touched * (w13 + w2) + w.T * (2 * w.H + 4 * w.E + 2 * w.H)
 
 
-def roofline(w, counts, stage_ms, path="auto"):
-    gemm1_ms = float(stage_ms[1])
+def roofline(w, counts, stage_ms, path="auto", kernel_ms=None):
+    """The dominant kernel's roofline.  Its time is kernel_ms, the mean duration
+    of the GEMM1 launch from the start and end events that launch carries
+    (no launch gaps, no stage events inside it); without it, the GEMM1 stage
+    time."""
+    gemm1_ms = float(kernel_ms) if kernel_ms is not None else float(stage_ms[1])
+    r = _roofline(w, counts, gemm1_ms, stage_ms, path)
+    r["kernel_us"] = round(gemm1_ms * 1e3, 2)
+    return r
+
+
+def _roofline(w, counts, gemm1_ms, stage_ms, path):
     if path == "one-kernel":
         # the whole layer in one kernel: its minimum bytes over its duration
         ms = float(sum(stage_ms))
@@ -292,12 +302,17 @@ def main():
     hip = Hip()
     nstage = m.NUM_STAGE_EVENTS
     ev = [(ctypes.c_void_p * nstage)(*[hip.event() for _ in range(nstage)]) for _ in range(a.steps)]
+    # the GEMM1 launch carries these two (its kernel's start and end times);
+    # the one-kernel layer has no separate GEMM1 launch
+    kev = ([(ctypes.c_void_p * 2)(hip.event(), hip.event()) for _ in range(a.steps)]
+           if a.gemm_path != "one-kernel" else None)
     flags = {"auto": m.FLAG_NONE, "narrow": m.FLAG_NARROW, "tiled": m.FLAG_TILED,
              "one-launch": m.FLAG_ONE_LAUNCH, "one-kernel": m.FLAG_ONE_KERNEL,
              "narrow-one-launch": m.FLAG_NARROW | m.FLAG_ONE_LAUNCH}[a.gemm_path]
     args_plain = m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, flags=flags)
     args_ev = [m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, flags=flags,
-                              stage_events=e) for e in ev]
+                              stage_events=e, kernel_events=kev[i] if kev else None)
+               for i, e in enumerate(ev)]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     if a.calib_copy_mb:
@@ -344,6 +359,8 @@ def main():
     stage_ms /= a.steps
     # spread of the step time over the stage pass (its events add a few us per step)
     step_ms = np.array([hip.elapsed_ms(e[0], e[nstage - 1]) for e in ev])
+    # the GEMM1 kernel's own duration, from the events its launch carries
+    kernel_ms = float(np.mean([hip.elapsed_ms(k[0], k[1]) for k in kev])) if kev else None
     tokens_s = w.T / (ms * 1e-3)
 
     counts = m.intermediates(d, ws)["counts"].cpu().numpy()
@@ -369,7 +386,7 @@ def main():
         "stages_ms": {n: round(float(v), 4) for n, v in zip(m.STAGES, stage_ms)},
         "stage_pass_step_ms": {q: round(float(np.percentile(step_ms, pq)), 4)
                                for q, pq in (("p10", 10), ("p50", 50), ("p90", 90))},
-        "roofline": roofline(w, counts, stage_ms, a.gemm_path),
+        "roofline": roofline(w, counts, stage_ms, a.gemm_path, kernel_ms),
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_experts)

@@ -123,7 +123,13 @@ typedef struct moe_dims {
  *             before the combine and after it (for per-stage timing); with
  *             MOE_FLAG_ONE_LAUNCH the third is recorded after that launch,
  *             right before the fourth; with MOE_FLAG_ONE_KERNEL the second,
- *             third and fourth are recorded after the one launch. */
+ *             third and fourth are recorded after the one launch.
+ *   kernel_events  NULL, or 2 caller-created HIP events that the GEMM1 launch
+ *             itself carries (hipExtLaunchKernel): they take the time the
+ *             GEMM1 kernel starts and the time it ends, so their elapsed time
+ *             is the kernel's duration without launch gaps (for rooflines).
+ *             With MOE_FLAG_ONE_LAUNCH they bracket the fused GEMM launch;
+ *             MOE_FLAG_ONE_KERNEL does not use them. */
 typedef struct moe_args {
     moe_dims_t dims;
     const uint16_t* x;
@@ -139,6 +145,7 @@ typedef struct moe_args {
     size_t ws_bytes;
     uint32_t flags;
     hipEvent_t* stage_events;
+    hipEvent_t* kernel_events;
 } moe_args_t;
 
 /* Byte offsets of the intermediates inside the workspace after moe_forward

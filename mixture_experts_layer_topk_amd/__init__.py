@@ -39,7 +39,7 @@ class Args(ctypes.Structure):
                 ("w13", ctypes.c_void_p), ("w13_sf", ctypes.c_void_p),
                 ("w2", ctypes.c_void_p), ("w2_sf", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32),
-                ("stage_events", ctypes.c_void_p)]
+                ("stage_events", ctypes.c_void_p), ("kernel_events", ctypes.c_void_p)]
 
 NUM_STAGE_EVENTS = 5
 STAGES = ("route+quant", "gemm1", "gemm2", "combine")
@@ -180,11 +180,14 @@ def route(d: Dims, logits: torch.Tensor, ws: torch.Tensor):
 
 
 def forward_args(d: Dims, x, w13, w13_sf, w2, w2_sf, y, ws, logits=None, topk_idx=None,
-                 topk_w=None, flags=0, stage_events=None) -> Args:
-    """stage_events: None or a ctypes array of NUM_STAGE_EVENTS hipEvent_t handles."""
+                 topk_w=None, flags=0, stage_events=None, kernel_events=None) -> Args:
+    """stage_events: None or a ctypes array of NUM_STAGE_EVENTS hipEvent_t handles;
+    kernel_events: None or a ctypes array of 2 handles that take the GEMM1 kernel's
+    start and end times."""
     ev = ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None
+    kev = ctypes.cast(kernel_events, ctypes.c_void_p) if kernel_events is not None else None
     return Args(d, _ptr(x), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(w13), _ptr(w13_sf),
-                _ptr(w2), _ptr(w2_sf), _ptr(y), _ptr(ws), ws.numel(), flags, ev)
+                _ptr(w2), _ptr(w2_sf), _ptr(y), _ptr(ws), ws.numel(), flags, ev, kev)
 
 
 def forward_raw(args: Args, stream=None):

@@ -337,12 +337,16 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     if ((a->flags & MOE_FLAG_ONE_LAUNCH) && !(a->flags & MOE_FLAG_NARROW)) narrow = false;
     const bool fused = (a->flags & MOE_FLAG_ONE_LAUNCH) != 0;
     if (ev) err = hipEventRecord(ev[1], s);
+    hipEvent_t* kev = a->kernel_events;
+    hipEvent_t k0 = kev ? kev[0] : nullptr, k1 = kev ? kev[1] : nullptr;
     if (fused) {
         // GEMM1 -> SwiGLU -> GEMM2 in one launch: both events after it
-        if (err == hipSuccess) err = narrow ? moe::launch_narrow_fused(gp, s) : moe::launch_fused_gemm(gp, s);
+        if (err == hipSuccess)
+            err = narrow ? moe::launch_narrow_fused(gp, s, k0, k1) : moe::launch_fused_gemm(gp, s, k0, k1);
         if (err == hipSuccess && ev) err = hipEventRecord(ev[2], s);
     } else {
-        if (err == hipSuccess) err = narrow ? moe::launch_narrow_gemm1(gp, s) : moe::launch_gemm1(gp, s);
+        if (err == hipSuccess)
+            err = narrow ? moe::launch_narrow_gemm1(gp, s, k0, k1) : moe::launch_gemm1(gp, s, k0, k1);
         if (err == hipSuccess && ev) err = hipEventRecord(ev[2], s);
         if (err == hipSuccess) err = narrow ? moe::launch_narrow_gemm2(gp, s) : moe::launch_gemm2(gp, s);
     }

@@ -807,7 +807,7 @@ static int device_cus() {
 }
 
 template <bool kG1>
-static hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
+static hipError_t launch_gemm(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     using C = Cfg<kBM, kBN, kWM, kWN, kG1>;
     auto kern = grouped_gemm_kernel<kBM, kBN, kWM, kWN, kG1>;
     const size_t lds = (size_t)C::kLds;
@@ -823,14 +823,18 @@ static hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     const int ntiles = kG1 ? (p.I + kBN / 2 - 1) / (kBN / 2) : (p.H + kBN - 1) / kBN;
     const int64_t upper = (int64_t)p.max_mtiles * ntiles;
     const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(upper, cus));
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), lds, s, p);
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), lds, s, ev0, ev1, 0, p);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm1(const GemmParams& p, hipStream_t s) { return launch_gemm<true>(p, s); }
-hipError_t launch_gemm2(const GemmParams& p, hipStream_t s) { return launch_gemm<false>(p, s); }
+hipError_t launch_gemm1(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    return launch_gemm<true>(p, s, ev0, ev1);
+}
+hipError_t launch_gemm2(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    return launch_gemm<false>(p, s, ev0, ev1);
+}
 
-hipError_t launch_fused_gemm(const GemmParams& p_in, hipStream_t s) {
+hipError_t launch_fused_gemm(const GemmParams& p_in, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     using C = Cfg<kBM, kBN, kWM, kWN, true>;
     auto kern = fused_gemm_kernel<kBM, kBN, kWM, kWN>;
     const size_t lds = (size_t)C::kLds;
@@ -856,7 +860,7 @@ hipError_t launch_fused_gemm(const GemmParams& p_in, hipStream_t s) {
     // tile of any other workgroup
     const int64_t upper = (int64_t)p.max_mtiles * (nt1 + nt2);
     const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(upper, cus));
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), lds, s, p);
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), lds, s, ev0, ev1, 0, p);
     return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Kernel parameter blocks and launchers (internal to the library).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -94,15 +95,30 @@ struct GemmParams {
 };
 
 int gemm_bm();                  // rows per m-tile of the grouped GEMMs
-hipError_t launch_gemm1(const GemmParams& p, hipStream_t s);
-hipError_t launch_gemm2(const GemmParams& p, hipStream_t s);
+
+// The GEMM launchers take an optional pair of events that the launch itself
+// carries (hipExtLaunchKernel): they take the kernel's start and end times.
+// A launcher with nothing to launch records them on the stream instead.
+inline hipError_t record_pair(hipEvent_t ev0, hipEvent_t ev1, hipStream_t s) {
+    hipError_t err = ev0 ? hipEventRecord(ev0, s) : hipSuccess;
+    if (err == hipSuccess && ev1) err = hipEventRecord(ev1, s);
+    return err;
+}
+hipError_t launch_gemm1(const GemmParams& p, hipStream_t s, hipEvent_t ev0 = nullptr,
+                        hipEvent_t ev1 = nullptr);
+hipError_t launch_gemm2(const GemmParams& p, hipStream_t s, hipEvent_t ev0 = nullptr,
+                        hipEvent_t ev1 = nullptr);
 // GEMM1 -> SwiGLU -> GEMM2 in one persistent launch with per-m-tile ready counters
-hipError_t launch_fused_gemm(const GemmParams& p, hipStream_t s);
+hipError_t launch_fused_gemm(const GemmParams& p, hipStream_t s, hipEvent_t ev0 = nullptr,
+                             hipEvent_t ev1 = nullptr);
 // the same two GEMMs for few rows per expert (decode): N split over many small
 // workgroups that stream weights straight into registers
-hipError_t launch_narrow_gemm1(const GemmParams& p, hipStream_t s);
-hipError_t launch_narrow_gemm2(const GemmParams& p, hipStream_t s);
-hipError_t launch_narrow_fused(const GemmParams& p, hipStream_t s);
+hipError_t launch_narrow_gemm1(const GemmParams& p, hipStream_t s, hipEvent_t ev0 = nullptr,
+                               hipEvent_t ev1 = nullptr);
+hipError_t launch_narrow_gemm2(const GemmParams& p, hipStream_t s, hipEvent_t ev0 = nullptr,
+                               hipEvent_t ev1 = nullptr);
+hipError_t launch_narrow_fused(const GemmParams& p, hipStream_t s, hipEvent_t ev0 = nullptr,
+                               hipEvent_t ev1 = nullptr);
 
 hipError_t launch_combine(const uint16_t* o, const int32_t* slot_of, int64_t T, int topk, int H,
                           uint16_t* y, hipStream_t s);

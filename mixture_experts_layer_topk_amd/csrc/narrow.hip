@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kNarrowThreads) void narrow_gemm_kernel(GemmParams 
 }
 
 template <bool kG1>
-static hipError_t launch_narrow(const GemmParams& p, hipStream_t s) {
+static hipError_t launch_narrow(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     static int cus = 0;
     if (cus == 0) {
         int dev = 0;
@@ -43,13 +43,18 @@ static hipError_t launch_narrow(const GemmParams& p, hipStream_t s) {
     const int nch = (kG1 ? p.I : p.H) / NarrowCfg<kG1>::kCols;
     const int64_t units = (int64_t)p.max_subs * nch;
     const int64_t grid = std::min<int64_t>(units, (int64_t)kNarrowBlocksPerCU * cus);
-    if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(narrow_gemm_kernel<kG1>, dim3((unsigned)grid), dim3(kNarrowThreads), 0, s, p);
+    if (grid <= 0) return record_pair(ev0, ev1, s);
+    hipExtLaunchKernelGGL(narrow_gemm_kernel<kG1>, dim3((unsigned)grid), dim3(kNarrowThreads), 0, s,
+                          ev0, ev1, 0, p);
     return hipGetLastError();
 }
 
-hipError_t launch_narrow_gemm1(const GemmParams& p, hipStream_t s) { return launch_narrow<true>(p, s); }
-hipError_t launch_narrow_gemm2(const GemmParams& p, hipStream_t s) { return launch_narrow<false>(p, s); }
+hipError_t launch_narrow_gemm1(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    return launch_narrow<true>(p, s, ev0, ev1);
+}
+hipError_t launch_narrow_gemm2(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    return launch_narrow<false>(p, s, ev0, ev1);
+}
 
 // GEMM1 -> SwiGLU -> GEMM2 of the narrow kernels in one launch: every
 // workgroup runs its GEMM1 units, then its GEMM2 units, whose activation loads
@@ -64,7 +69,7 @@ __global__ __launch_bounds__(kNarrowThreads) void narrow_fused_kernel(GemmParams
     narrow_gemm<false, true>(p, blockIdx.x, gridDim.x);
 }
 
-hipError_t launch_narrow_fused(const GemmParams& p, hipStream_t s) {
+hipError_t launch_narrow_fused(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     static int cus = 0, per_cu = 0;
     if (cus == 0) {
         int dev = 0, occ = 0;
@@ -83,8 +88,9 @@ hipError_t launch_narrow_fused(const GemmParams& p, hipStream_t s) {
     const int nch = std::max(p.I / NarrowCfg<true>::kCols, p.H / NarrowCfg<false>::kCols);
     const int64_t units = (int64_t)p.max_subs * nch;
     const int64_t grid = std::min<int64_t>(units, (int64_t)per_cu * cus);
-    if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(narrow_fused_kernel, dim3((unsigned)grid), dim3(kNarrowThreads), 0, s, p);
+    if (grid <= 0) return record_pair(ev0, ev1, s);
+    hipExtLaunchKernelGGL(narrow_fused_kernel, dim3((unsigned)grid), dim3(kNarrowThreads), 0, s, ev0, ev1,
+                          0, p);
     return hipGetLastError();
 }
 

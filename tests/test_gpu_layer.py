@@ -4,6 +4,7 @@ Integer outputs (routing ids, counts, offsets, slot multisets, FP8/FP4 codes
 and scales from the quantisers) must be bit-exact; floating-point outputs meet
 the tolerances stated in tests/gpu_common.py.
 """
+import ctypes
 import sys
 
 import numpy as np
@@ -398,3 +399,46 @@ def test_forward_zero_tokens_is_noop():
     m.forward_raw(m.forward_args(d, x, w, w, w, w, y, ws, logits=x))
     torch.cuda.synchronize()
     assert (y.float() == 7.0).all()
+
+
+@pytest.mark.parametrize("flags", ["tiled", "narrow", "one-launch", "narrow-one-launch"])
+def test_timing_events_leave_y_unchanged(flags):
+    """Stage events and the GEMM1 launch's own events change nothing in y; the
+    GEMM1 kernel's start-to-end time is positive and inside its stage."""
+    m = G.lib()
+    f = {"tiled": m.FLAG_TILED, "narrow": m.FLAG_NARROW, "one-launch": m.FLAG_ONE_LAUNCH,
+         "narrow-one-launch": m.FLAG_NARROW | m.FLAG_ONE_LAUNCH}[flags]
+    w = RAGGED
+    _log(f"timing events {flags}")
+    dl = G.DeviceLayer(w)
+    ref = G.y_bits(dl.forward(flags=f))
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event():
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000) == 0   # no system fence
+        return e
+
+    def elapsed(a, b):
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    sev = (ctypes.c_void_p * m.NUM_STAGE_EVENTS)(*[event() for _ in range(m.NUM_STAGE_EVENTS)])
+    kev = (ctypes.c_void_p * 2)(event(), event())
+    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    args = m.forward_args(dl.d, dl.x, dl.w13q, dl.w13sf_k, dl.w2q, dl.w2sf_k, y, dl.ws,
+                          logits=dl.logits, flags=f, stage_events=sev, kernel_events=kev)
+    for _ in range(2):
+        m.forward_raw(args)
+        torch.cuda.synchronize()
+        assert np.array_equal(G.y_bits(y), ref)
+        kernel = elapsed(kev[0], kev[1])
+        stage = elapsed(sev[1], sev[2])
+        assert 0.0 < kernel <= stage + 1e-3, (kernel, stage)
+    for e in list(sev) + list(kev):
+        hip.hipEventDestroy(e)

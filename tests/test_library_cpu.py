@@ -96,3 +96,32 @@ def test_error_strings():
     m = _lib()
     for code in (0, -1, -2, -3, -4, -99):
         assert m._lib.moe_error_string(code)
+
+
+def test_ctypes_structs_match_the_c_header(tmp_path):
+    """The binding's ctypes structs have the header's field offsets and sizes
+    (a host-only C program built against include/moe.h prints them)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc")
+    if cc is None or not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("needs gcc and the HIP headers")
+    m = _lib()
+    structs = {"moe_dims_t": m.Dims, "moe_args_t": m.Args, "moe_layout_t": m.Layout}
+    lines = ['#include <stdio.h>', '#include "moe.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l}
+    for cname, py in structs.items():
+        assert got[(cname, "sizeof")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
