@@ -788,22 +788,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams 
     }
 }
 
-// Tile configuration: 128 x 512 output tiles, 4 waves of 128 x 128 side by
-// side.  128-row m-tiles waste fewer padding rows on ragged expert segments
-// than 256-row ones; the LDS and MFMA work per K step are those of 256 x 256.
+// Tile configuration: 128 x 512 output tiles over 8 waves, 2 rows x 4 columns
+// of 64 x 128 wave tiles (the wave in row 1 is the late one of its SIMD).
+// 128-row m-tiles waste fewer padding rows on ragged expert segments than
+// 256-row ones, at the MFMA work per K step of a 256 x 256 tile.
 constexpr int kBM = 128, kBN = 512, kWM = 2, kWN = 4;
 
 int gemm_bm() { return kBM; }
 
-static int device_cus() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 0;
-    }
-    return cus;
+// The kernels take more than the default dynamic LDS: raise the limit once per device.
+static hipError_t allow_lds(const void* kern, int bytes, DeviceCache& done) {
+    int ok = 0;
+    return per_device(done, [&](int, int* v) {
+        hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        *v = 1;
+        return err;
+    }, &ok);
 }
 
 template <bool kG1>
@@ -811,14 +811,11 @@ static hipError_t launch_gemm(const GemmParams& p, hipStream_t s, hipEvent_t ev0
     using C = Cfg<kBM, kBN, kWM, kWN, kG1>;
     auto kern = grouped_gemm_kernel<kBM, kBN, kWM, kWN, kG1>;
     const size_t lds = (size_t)C::kLds;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute((const void*)kern,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (err != hipSuccess) return err;
-        attr_set = true;
-    }
-    const int cus = device_cus();
+    static DeviceCache lds_set;
+    hipError_t err = allow_lds((const void*)kern, (int)lds, lds_set);
+    int cus = 0;
+    if (err == hipSuccess) err = device_cus(&cus);
+    if (err != hipSuccess) return err;
     if (cus <= 0) return hipErrorInvalidDevice;
     const int ntiles = kG1 ? (p.I + kBN / 2 - 1) / (kBN / 2) : (p.H + kBN - 1) / kBN;
     const int64_t upper = (int64_t)p.max_mtiles * ntiles;
@@ -838,14 +835,11 @@ hipError_t launch_fused_gemm(const GemmParams& p_in, hipStream_t s, hipEvent_t e
     using C = Cfg<kBM, kBN, kWM, kWN, true>;
     auto kern = fused_gemm_kernel<kBM, kBN, kWM, kWN>;
     const size_t lds = (size_t)C::kLds;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute((const void*)kern,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (err != hipSuccess) return err;
-        attr_set = true;
-    }
-    const int cus = device_cus();
+    static DeviceCache lds_set;
+    hipError_t err = allow_lds((const void*)kern, (int)lds, lds_set);
+    int cus = 0;
+    if (err == hipSuccess) err = device_cus(&cus);
+    if (err != hipSuccess) return err;
     if (cus <= 0) return hipErrorInvalidDevice;
     GemmParams p = p_in;
     // experts per wave: enough GEMM1 tiles to give every CU about two

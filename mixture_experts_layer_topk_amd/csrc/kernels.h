@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 namespace moe {
 
@@ -95,6 +96,34 @@ struct GemmParams {
 };
 
 int gemm_bm();                  // rows per m-tile of the grouped GEMMs
+
+// Launch facts cached per device (CU counts, occupancies, "attribute set"):
+// the entry for the current device is filled by fill(dev, &value) on first use.
+// 0 means "not cached", so a fill that yields 0 runs again next time.  Host
+// threads may race on the first fill; they compute the same value.
+constexpr int kMaxDevices = 64;
+using DeviceCache = std::atomic<int>[kMaxDevices];
+template <class F>
+hipError_t per_device(DeviceCache& cache, F fill, int* out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        err = fill(dev, &v);
+        if (err != hipSuccess) return err;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    *out = v;
+    return hipSuccess;
+}
+inline hipError_t device_cus(int* cus) {
+    static DeviceCache cache;
+    return per_device(cache, [](int dev, int* v) {
+        return hipDeviceGetAttribute(v, hipDeviceAttributeMultiprocessorCount, dev);
+    }, cus);
+}
 
 // The GEMM launchers take an optional pair of events that the launch itself
 // carries (hipExtLaunchKernel): they take the kernel's start and end times.

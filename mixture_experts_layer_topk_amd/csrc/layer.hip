@@ -111,18 +111,14 @@ bool layer_small_fits(int64_t T, int topk) { return T > 0 && T * topk <= kSmallP
 
 hipError_t launch_layer_small(const RouteParams& rp, const ScatterParams& sp, const GemmParams& gp,
                               LayerParams lp, hipStream_t s) {
-    static int cus = 0, per_cu = 0;
-    if (cus == 0) {
-        int dev = 0;
-        hipError_t err = hipGetDevice(&dev);
-        if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (err == hipSuccess)
-            err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, layer_small_kernel, kLayerThreads, 0);
-        if (err != hipSuccess) {
-            cus = 0;
-            return err;
-        }
-    }
+    static DeviceCache occupancy;
+    int cus = 0, per_cu = 0;
+    hipError_t err = device_cus(&cus);
+    if (err == hipSuccess)
+        err = per_device(occupancy, [](int, int* v) {
+            return hipOccupancyMaxActiveBlocksPerMultiprocessor(v, layer_small_kernel, kLayerThreads, 0);
+        }, &per_cu);
+    if (err != hipSuccess) return err;
     if (per_cu < 1) return hipErrorInvalidConfiguration;
     lp.npl = rp.logits ? (rp.E + 63) / 64 : 1;
     // two workgroups per CU, as the narrow GEMM launches use

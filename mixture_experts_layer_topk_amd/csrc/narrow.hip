@@ -32,14 +32,9 @@ __global__ __launch_bounds__(kNarrowThreads) void narrow_gemm_kernel(GemmParams 
 
 template <bool kG1>
 static hipError_t launch_narrow(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        hipError_t err = hipGetDevice(&dev);
-        if (err == hipSuccess)
-            err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (err != hipSuccess) return err;
-    }
+    int cus = 0;
+    hipError_t err = device_cus(&cus);
+    if (err != hipSuccess) return err;
     const int nch = (kG1 ? p.I : p.H) / NarrowCfg<kG1>::kCols;
     const int64_t units = (int64_t)p.max_subs * nch;
     const int64_t grid = std::min<int64_t>(units, (int64_t)kNarrowBlocksPerCU * cus);
@@ -70,20 +65,15 @@ __global__ __launch_bounds__(kNarrowThreads) void narrow_fused_kernel(GemmParams
 }
 
 hipError_t launch_narrow_fused(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    static int cus = 0, per_cu = 0;
-    if (cus == 0) {
-        int dev = 0, occ = 0;
-        hipError_t err = hipGetDevice(&dev);
-        if (err == hipSuccess)
-            err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (err == hipSuccess)
-            err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, narrow_fused_kernel, kNarrowThreads, 0);
-        if (err != hipSuccess) {
-            cus = 0;
-            return err;
-        }
-        per_cu = std::min(occ, kNarrowBlocksPerCU);
-    }
+    static DeviceCache occupancy;
+    int cus = 0, per_cu = 0;
+    hipError_t err = device_cus(&cus);
+    if (err == hipSuccess)
+        err = per_device(occupancy, [](int, int* v) {
+            return hipOccupancyMaxActiveBlocksPerMultiprocessor(v, narrow_fused_kernel, kNarrowThreads, 0);
+        }, &per_cu);
+    if (err != hipSuccess) return err;
+    per_cu = std::min(per_cu, kNarrowBlocksPerCU);
     if (per_cu < 1) return hipErrorInvalidConfiguration;
     const int nch = std::max(p.I / NarrowCfg<true>::kCols, p.H / NarrowCfg<false>::kCols);
     const int64_t units = (int64_t)p.max_subs * nch;
