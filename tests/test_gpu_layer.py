@@ -401,14 +401,16 @@ def test_forward_zero_tokens_is_noop():
     assert (y.float() == 7.0).all()
 
 
-@pytest.mark.parametrize("flags", ["tiled", "narrow", "one-launch", "narrow-one-launch"])
+@pytest.mark.parametrize("flags", ["tiled", "narrow", "one-launch", "narrow-one-launch", "one-kernel"])
 def test_timing_events_leave_y_unchanged(flags):
     """Stage events and the GEMM1 launch's own events change nothing in y; the
-    GEMM1 kernel's start-to-end time is positive and inside its stage."""
+    GEMM1 kernel's start-to-end time is positive and inside its stage.  The
+    one-kernel layer records its stage events and leaves the kernel pair alone."""
     m = G.lib()
     f = {"tiled": m.FLAG_TILED, "narrow": m.FLAG_NARROW, "one-launch": m.FLAG_ONE_LAUNCH,
-         "narrow-one-launch": m.FLAG_NARROW | m.FLAG_ONE_LAUNCH}[flags]
-    w = RAGGED
+         "narrow-one-launch": m.FLAG_NARROW | m.FLAG_ONE_LAUNCH,
+         "one-kernel": m.FLAG_ONE_KERNEL}[flags]
+    w = W.WORKLOADS["decode"] if flags == "one-kernel" else RAGGED
     _log(f"timing events {flags}")
     dl = G.DeviceLayer(w)
     ref = G.y_bits(dl.forward(flags=f))
@@ -437,8 +439,10 @@ def test_timing_events_leave_y_unchanged(flags):
         m.forward_raw(args)
         torch.cuda.synchronize()
         assert np.array_equal(G.y_bits(y), ref)
-        kernel = elapsed(kev[0], kev[1])
-        stage = elapsed(sev[1], sev[2])
-        assert 0.0 < kernel <= stage + 1e-3, (kernel, stage)
+        stages = [elapsed(sev[i], sev[i + 1]) for i in range(m.NUM_STAGE_EVENTS - 1)]
+        assert all(t >= 0.0 for t in stages) and sum(stages) > 0.0, stages
+        if flags != "one-kernel":
+            kernel = elapsed(kev[0], kev[1])
+            assert 0.0 < kernel <= stages[1] + 1e-3, (kernel, stages)
     for e in list(sev) + list(kev):
         hip.hipEventDestroy(e)
