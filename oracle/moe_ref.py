@@ -34,6 +34,8 @@ float32, as the pages do.
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from . import codecs as C
@@ -133,6 +135,28 @@ def pack_weights(w_bf16_bits):
     return C.pack_e2m1(codes), sf
 
 
+def interleave_w13(w13q, w13sf, gran: int = 8):
+    """The pages' offline gate/up row interleave of W13 ([MegaMoE notes]
+    "原始权重布局", "_interleave_l1_weights" with gran = 8): the canonical rows are
+    gate [0, I) then up [I, 2I); the interleaved rows alternate blocks of ``gran``
+    gate rows and the ``gran`` up rows of the same columns, so rows
+    [2 gran i, 2 gran i + gran) are gate rows [gran i, gran i + gran) and rows
+    [2 gran i + gran, 2 gran (i + 1)) are up rows [gran i, gran i + gran).
+    Works on codes [..., 2I, H/2] and per-row scales [..., 2I, H/32] alike."""
+    out = []
+    for a in (np.asarray(w13q), np.asarray(w13sf)):
+        two_i = a.shape[-2]
+        I = two_i // 2
+        assert two_i % 2 == 0 and I % gran == 0
+        b = np.empty_like(a)
+        for i in range(I // gran):
+            g0 = gran * i
+            b[..., 2 * g0:2 * g0 + gran, :] = a[..., g0:g0 + gran, :]
+            b[..., 2 * g0 + gran:2 * g0 + 2 * gran, :] = a[..., I + g0:I + g0 + gran, :]
+        out.append(b)
+    return out[0], out[1]
+
+
 def dequant_weights(packed, sf) -> np.ndarray:
     return C.dequantize_blocks(C.unpack_e2m1(packed), sf, "e2m1")
 
@@ -183,13 +207,16 @@ def combine(o_bf16, slot_of) -> np.ndarray:
 
 
 def forward(x_bf16_bits, w13q, w13sf, w2q, w2sf, *, topk, I, logits=None,
-            topk_idx=None, topk_w=None, score_fn=SOFTMAX, renorm=True, tokens=None):
+            topk_idx=None, topk_w=None, score_fn=SOFTMAX, renorm=True, tokens=None,
+            workers=None):
     """Whole layer.  Either ``logits`` [T, E] or ``topk_idx``/``topk_w`` [T, k].
 
     Weights are already quantised: w13q [E, 2I, H/2], w13sf [E, 2I, H/32],
     w2q [E, H, I/2], w2sf [E, H, I/32] (indexable by expert; a dict works).
     ``tokens`` restricts GEMMs and combine to those tokens (routing and
     bucketisation still cover all tokens); y rows of other tokens are zero.
+    ``workers`` > 1 runs the per-expert steps on that many threads (each expert
+    writes its own rows; the arithmetic is the same).
     Returns a dict of every intermediate.
     """
     x = np.asarray(x_bf16_bits, dtype=np.uint16)
@@ -213,15 +240,22 @@ def forward(x_bf16_bits, w13q, w13sf, w2q, w2sf, *, topk, I, logits=None,
     hq = np.zeros((N, I), np.uint8)
     hsf = np.zeros((N, I // 32), np.uint8)
     o = np.zeros((N, H), np.uint16)
-    for e in range(E):
+    def one_expert(e):
         pos = np.arange(offsets[e], offsets[e + 1])
         pos = pos[want[pos]]
         if pos.size == 0:
-            continue
+            return
         f = slot_src[pos]
         t, j = f // topk, f % topk
         hq[pos], hsf[pos], _, o[pos] = expert_rows(
             xq[t], xsf[t], topk_w[t, j], w13q[e], w13sf[e], w2q[e], w2sf[e], I)
+
+    if workers and workers > 1:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one_expert, range(E)))
+    else:
+        for e in range(E):
+            one_expert(e)
     so = slot_of.copy()
     if tokens is not None:
         so[~sel] = -1

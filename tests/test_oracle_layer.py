@@ -226,9 +226,33 @@ def test_token_subset_matches_full_forward():
 
 
 def test_combine_adds_in_slot_order_in_fp32():
-    # 1 + 2^-24 + 2^-24 in fp32, slot order: each add rounds back to 1
-    o = C.bf16_bits(np.array([[1.0], [2.0 ** -24], [2.0 ** -24]], np.float32))
-    y = M.combine(o, np.array([[0, 1, 2]]))
+    """y[t] = BF16 of the float32 sum of the token's rows in slot order j = 0..k-1
+    ([MegaMoE notes] "L2 epilogue"; the q6 reading).  With rows 1, 2^-8, 2^-24,
+    2^-24 (all BF16), the float32 sum in slot order stays at 1 + 2^-8: each
+    2^-24 is half a float32 ulp there and rounds back to the even neighbour.  That
+    is the midpoint of BF16 1 and 1 + 2^-7, which rounds to the even 1.0.  Adding
+    the same rows in reverse order (2^-24 + 2^-24 = 2^-23 first) or exactly gives
+    1 + 2^-8 + 2^-23, above the midpoint: BF16 1 + 2^-7."""
+    vals = np.array([[1.0], [2.0 ** -8], [2.0 ** -24], [2.0 ** -24]], np.float32)
+    o = C.bf16_bits(vals)
+    assert np.array_equal(C.bf16_value(o), vals)             # the rows are BF16 values
+    y = M.combine(o, np.array([[0, 1, 2, 3]]))
     assert C.bf16_value(y)[0, 0] == 1.0
-    y2 = M.combine(o, np.array([[1, 2, 0]]))       # small terms first: still 1 after BF16
-    assert C.bf16_value(y2)[0, 0] == 1.0
+    y_rev = M.combine(o, np.array([[3, 2, 1, 0]]))             # the same rows, slots reversed
+    assert C.bf16_value(y_rev)[0, 0] == 1.0 + 2.0 ** -7
+
+
+def test_interleave_w13_matches_the_pages_layout():
+    """[MegaMoE notes] "原始权重布局": after the gran = 8 interleave the N dimension
+    reads gate0 (8 rows), up0 (8), gate1 (8), up1 (8), ...; every 8 gate rows are
+    followed by the 8 up rows of the same columns."""
+    I = 32
+    rows = np.arange(2 * I, dtype=np.int64)
+    q = np.repeat(rows[None, :, None], 3, axis=2)           # [1, 2I, 3], row r holds r
+    sf = np.repeat(rows[None, :, None], 2, axis=2)
+    iq, isf = M.interleave_w13(q, sf)
+    expect = np.concatenate([np.r_[8 * i:8 * i + 8, I + 8 * i:I + 8 * i + 8] for i in range(I // 8)])
+    assert np.array_equal(iq[0, :, 0], expect)
+    assert np.array_equal(isf[0, :, 1], expect)
+    assert list(expect[:32]) == list(range(0, 8)) + list(range(32, 40)) + list(range(8, 16)) + list(range(40, 48))
+    assert np.array_equal(np.sort(expect), rows)             # a permutation of the rows

@@ -108,3 +108,27 @@ def test_wrong_nibble_order_is_caught(monkeypatch):
     monkeypatch.setattr(C, "pack_e2m1", lambda c: (np.asarray(c)[..., 1::2] & 0xF) | ((np.asarray(c)[..., 0::2] & 0xF) << 4))
     with pytest.raises(AssertionError):
         TC.test_fp4_pack_roundtrip_and_nibble_order()
+
+
+def _combine_f64(o_bf16, slot_of):
+    slot_of = np.asarray(slot_of)
+    T, k = slot_of.shape
+    acc = np.zeros((T, o_bf16.shape[1]), np.float64)
+    for j in range(k):
+        p = slot_of[:, j]
+        acc[p >= 0] += C.bf16_value(o_bf16[p[p >= 0]])
+    return C.bf16_bits(acc.astype(np.float32))
+
+
+def _combine_reversed(o_bf16, slot_of):
+    return _ORIG_COMBINE(o_bf16, np.asarray(slot_of)[:, ::-1])
+
+
+_ORIG_COMBINE = M.combine
+
+
+@pytest.mark.parametrize("patch", [_combine_f64, _combine_reversed], ids=["float64_sum", "reversed_slots"])
+def test_combine_order_and_precision_mistakes_are_caught(monkeypatch, patch):
+    monkeypatch.setattr(M, "combine", patch)
+    with pytest.raises(AssertionError):
+        TL.test_combine_adds_in_slot_order_in_fp32()
