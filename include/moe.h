@@ -19,8 +19,8 @@
  * Conventions for every entry point:
  *   - Pointers marked "device" are device memory owned by the caller; the
  *     library never allocates, frees or keeps them.  Work is enqueued on the
- *     given HIP stream; no call synchronises with the host.  Results are valid
- *     once the stream has reached the call.
+ *     given HIP stream; no call but moe_check_status synchronises with the
+ *     host.  Results are valid once the stream has reached the call.
  *   - Return 0 on success or a negative MOE_E* code.  Argument errors are
  *     detected on the host before anything is enqueued.  A kernel launch error
  *     returns MOE_EHIP; moe_error_string(MOE_EHIP) then holds the HIP message
@@ -47,6 +47,7 @@ extern "C" {
 #define MOE_EUNSUPPORTED (-2)  /* shape outside what the kernels handle */
 #define MOE_EWORKSPACE (-3)    /* workspace too small or misaligned */
 #define MOE_EHIP (-4)          /* HIP runtime / launch failure */
+#define MOE_ETIMEOUT (-5)      /* moe_check_status: a bounded wait inside the last call gave up */
 
 #define MOE_SCORE_SOFTMAX 0
 #define MOE_SCORE_SIGMOID 1
@@ -100,6 +101,35 @@ typedef struct moe_dims {
 #define MOE_FLAG_TILED 2u
 #define MOE_FLAG_ONE_LAUNCH 4u
 #define MOE_FLAG_ONE_KERNEL 8u
+/* Weight-layout and debugging flags ("MegaMoE：把通信和计算融合到一个 Mega Kernel",
+ * Python API walk-through: the caller transforms the weights once, then makes
+ * one call per batch; "MonoMoe kernel — design" §2-§3 for bounded waits):
+ *   W13_PREINTERLEAVED  w13 (codes and scales) is in the pages' gate/up row
+ *                       interleave with granularity 8 ("MegaMoE" study notes,
+ *                       "原始权重布局"): rows [16 i, 16 i + 8) are gate rows
+ *                       [8 i, 8 i + 8) and rows [16 i + 8, 16 i + 16) the up
+ *                       rows of the same 8 columns.  Without it, rows [0, I)
+ *                       are gate and [I, 2I) up.  Results are bit-identical.
+ *   W_SCALES_PER_ROW    w13_sf and w2_sf are per-row [E, rows, K/32] (as
+ *                       moe_pack_weights writes them) instead of K-step major
+ *                       [E, K/128, rows, 4].  Results are bit-identical; the
+ *                       per-row layout costs one load per scale row and K step
+ *                       instead of one per 64 rows.
+ *   KEEP_INTERMEDIATES  accepted for callers that state it: every call leaves
+ *                       its intermediates in the workspace at the offsets
+ *                       moe_workspace_layout reports, until the next call.
+ *   DEBUG_SPIN_BOUND    the ready-counter waits of the one-launch GEMM paths
+ *                       give up after one failed poll instead of about 0.5 s
+ *                       of polling; a wait that gives up sets the status word
+ *                       (moe_check_status reports MOE_ETIMEOUT) and the output
+ *                       is then invalid.  For exercising the failure report;
+ *                       MOE_EINVAL together with ONE_KERNEL, whose grid
+ *                       barriers guard the routing tables the later phases
+ *                       index with. */
+#define MOE_FLAG_W13_PREINTERLEAVED 16u
+#define MOE_FLAG_W_SCALES_PER_ROW 32u
+#define MOE_FLAG_KEEP_INTERMEDIATES 64u
+#define MOE_FLAG_DEBUG_SPIN_BOUND 128u
 
 #define MOE_NUM_STAGE_EVENTS 5
 
@@ -110,9 +140,11 @@ typedef struct moe_dims {
  *   topk_w    device, float32 [T, topk] routing weights
  *   w13       device, FP4 [E, 2I, H/2]: rows [0, I) gate (W1), [I, 2I) up (W3)
  *   w13_sf    device, UE8M0 [E, H/128, 2I, 4]: K-step major (moe_scales_kmajor
- *             of the per-row [E, 2I, H/32] scales)
+ *             of the per-row [E, 2I, H/32] scales); per-row [E, 2I, H/32]
+ *             with MOE_FLAG_W_SCALES_PER_ROW
  *   w2        device, FP4 [E, H, I/2]
- *   w2_sf     device, UE8M0 [E, I/128, H, 4]: K-step major
+ *   w2_sf     device, UE8M0 [E, I/128, H, 4]: K-step major; per-row
+ *             [E, H, I/32] with MOE_FLAG_W_SCALES_PER_ROW
  *   y         device, BF16 [T, H], written
  *   ws        device workspace of at least moe_workspace_size() bytes,
  *             256-byte aligned, zeroed once by moe_workspace_init() after it is
@@ -171,10 +203,17 @@ typedef struct moe_layout {
     size_t total;
 } moe_layout_t;
 
-/* Size in bytes of the workspace moe_forward and moe_route need for d. */
+/* Size in bytes of the caller-owned workspace moe_forward and moe_route need
+ * for d ("MonoMoe kernel — design" §4: the host sizes the scratchpad from the
+ * library, which exports its size; "MegaMoE" study notes, "WorkSpace").
+ *   d      host pointer to the shape (checked as for moe_forward)
+ *   bytes  host pointer, out
+ * Returns MOE_EINVAL / MOE_EUNSUPPORTED for a bad shape, else MOE_OK. */
 int moe_workspace_size(const moe_dims_t* d, size_t* bytes);
 
-/* Offsets of the intermediates in the workspace for d. */
+/* Offsets of the intermediates in the workspace for d (the same pages as
+ * moe_workspace_size).  d and out are host pointers; errors as for
+ * moe_workspace_size. */
 int moe_workspace_layout(const moe_dims_t* d, moe_layout_t* out);
 
 /* Zero a freshly allocated workspace (enqueued on s).  Needed once per
@@ -228,9 +267,29 @@ int moe_pack_weights(const uint16_t* w, int64_t rows, int32_t cols, uint8_t* q, 
 int moe_scales_kmajor(const uint8_t* sf, int64_t mats, int32_t rows, int32_t cols, uint8_t* out,
                       hipStream_t s);
 
-/* The whole layer: route (or take topk_idx/topk_w), bucketise, quantise x,
- * GEMM1 + SwiGLU*weight -> FP8, GEMM2 -> BF16, combine into y. */
+/* The whole layer ("MegaMoE" study notes, "Dispatch阶段" flow chart: route or
+ * take topk_idx/topk_w, counting-sort bucketisation, quantise x, GEMM1 +
+ * SwiGLU*weight -> FP8, GEMM2 -> BF16, combine into y; "MegaMoE：把通信和计算
+ * 融合到一个 Mega Kernel", Python API walk-through: one call per batch on a
+ * caller-allocated workspace and transformed weights).
+ *   a  host pointer to the arguments (moe_args_t above); every tensor in it is
+ *      device memory owned by the caller.
+ * Returns MOE_EINVAL for a NULL or misaligned pointer (x, w13, w2, y 16-byte
+ * aligned; scales 4-byte aligned), an unknown or contradictory flag set;
+ * MOE_EUNSUPPORTED for a shape outside moe_dims_t's limits; MOE_EWORKSPACE
+ * for a workspace below moe_workspace_size or not 256-byte aligned; MOE_EHIP
+ * for a launch failure.  T == 0 returns MOE_OK without launching. */
 int moe_forward(const moe_args_t* a, hipStream_t s);
+
+/* Status of the last call on workspace ws ("MonoMoe kernel — design" §2-§3:
+ * waits are bounded so a broken hand-off ends instead of hanging).
+ * Synchronises stream s (waits for every call enqueued on it), then reads the
+ * status word at its fixed offset in the workspace header (the same for every
+ * shape).  Returns MOE_OK, or MOE_ETIMEOUT when a bounded wait of the last
+ * moe_forward on ws gave up (its output is then invalid; never in a correct
+ * run without MOE_FLAG_DEBUG_SPIN_BOUND), or MOE_EINVAL for a NULL or
+ * misaligned ws, or MOE_EHIP. */
+int moe_check_status(const void* ws, hipStream_t s);
 
 /* Static text for a return code (for MOE_EHIP: the calling thread's last HIP
  * error message). */

@@ -17,8 +17,11 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_ETIMEOUT = -5
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 FLAG_NONE, FLAG_NARROW, FLAG_TILED, FLAG_ONE_LAUNCH, FLAG_ONE_KERNEL = 0, 1, 2, 4, 8
+FLAG_W13_PREINTERLEAVED, FLAG_W_SCALES_PER_ROW = 16, 32
+FLAG_KEEP_INTERMEDIATES, FLAG_DEBUG_SPIN_BOUND = 64, 128
 
 
 class MoeError(RuntimeError):
@@ -54,7 +57,7 @@ class Layout(ctypes.Structure):
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_workspace_size", "moe_workspace_layout", "moe_workspace_init", "moe_route",
            "moe_quant_act", "moe_pack_weights", "moe_scales_kmajor", "moe_forward",
-           "moe_error_string")
+           "moe_check_status", "moe_error_string")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -71,6 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_pack_weights.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_scales_kmajor.argtypes = [vp, i64, i32, i32, vp, vp]
     lib.moe_forward.argtypes = [ctypes.POINTER(Args), vp]
+    lib.moe_check_status.argtypes = [vp, vp]
     lib.moe_error_string.argtypes = [ctypes.c_int]
     lib.moe_error_string.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -206,6 +210,15 @@ def forward(d: Dims, x, w13, w13_sf, w2, w2_sf, ws, logits=None, topk_idx=None, 
     forward_raw(forward_args(d, x, w13, w13_sf, w2, w2_sf, y, ws, logits, topk_idx, topk_w,
                              flags=flags))
     return y
+
+
+def check_status(ws: torch.Tensor) -> int:
+    """Synchronise the current stream and return MOE_OK, or MOE_ETIMEOUT when a
+    bounded wait of the last forward on ws gave up (errors raise)."""
+    rc = _lib.moe_check_status(_ptr(ws), _stream())
+    if rc not in (MOE_OK, MOE_ETIMEOUT):
+        _check(rc)
+    return rc
 
 
 def intermediates(d: Dims, ws: torch.Tensor):

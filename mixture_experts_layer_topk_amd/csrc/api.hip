@@ -229,9 +229,12 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     if (!a->x || !a->w13 || !a->w13_sf || !a->w2 || !a->w2_sf || !a->y || !a->ws) return MOE_EINVAL;
     if (!a->logits && (!a->topk_idx || !a->topk_w)) return MOE_EINVAL;
     const uint32_t f = a->flags;
-    if ((f & ~(MOE_FLAG_NARROW | MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH | MOE_FLAG_ONE_KERNEL)) ||
-        ((f & MOE_FLAG_NARROW) && (f & MOE_FLAG_TILED)) ||
-        ((f & MOE_FLAG_ONE_KERNEL) && (f & (MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH))))
+    const uint32_t known = MOE_FLAG_NARROW | MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH | MOE_FLAG_ONE_KERNEL |
+                           MOE_FLAG_W13_PREINTERLEAVED | MOE_FLAG_W_SCALES_PER_ROW |
+                           MOE_FLAG_KEEP_INTERMEDIATES | MOE_FLAG_DEBUG_SPIN_BOUND;
+    if ((f & ~known) || ((f & MOE_FLAG_NARROW) && (f & MOE_FLAG_TILED)) ||
+        ((f & MOE_FLAG_ONE_KERNEL) &&
+         (f & (MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH | MOE_FLAG_DEBUG_SPIN_BOUND))))
         return MOE_EINVAL;
     if ((f & MOE_FLAG_ONE_KERNEL) && !moe::layer_small_fits(d.T, d.topk)) return MOE_EUNSUPPORTED;
     if (!aligned16(a->x) || !aligned16(a->w13) || !aligned16(a->w2) || !aligned16(a->y) ||
@@ -315,6 +318,18 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     gp.I = d.I;
     gp.E = d.E;
     gp.topk = d.topk;
+    // a bounded wait that gives up after one failed poll (DEBUG_SPIN_BOUND), else the kernels' own
+    gp.spin_limit = (f & MOE_FLAG_DEBUG_SPIN_BOUND) ? 1 : 0;
+    gp.w13_il = (f & MOE_FLAG_W13_PREINTERLEAVED) ? 1 : 0;
+    if (f & MOE_FLAG_W_SCALES_PER_ROW) {        // [E, rows, K/32]
+        gp.w13sf_rs = d.H / 32;
+        gp.w2sf_rs = d.I / 32;
+        gp.w13sf_ks = gp.w2sf_ks = 4;
+    } else {                                    // [E, K/128, rows, 4]
+        gp.w13sf_rs = gp.w2sf_rs = 4;
+        gp.w13sf_ks = 4 * 2 * (int64_t)d.I;
+        gp.w2sf_ks = 4 * (int64_t)d.H;
+    }
     const int64_t R = d.T * d.topk;
     gp.max_mtiles = (int)max_mtiles(d);
     gp.max_subs = (int)max_subs(d);
@@ -356,12 +371,26 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     return err == hipSuccess ? MOE_OK : hip_fail(err);
 }
 
+int moe_check_status(const void* ws, hipStream_t s) {
+    if (!ws || ((uintptr_t)ws % kAlign) != 0) return MOE_EINVAL;
+    // the header's offsets do not depend on the shape: any valid shape gives them
+    moe_dims_t one{1, 128, 128, 1, 1, MOE_SCORE_SOFTMAX, 1};
+    const Carve c = carve(one);
+    int status = 0;
+    hipError_t err = hipMemcpyAsync(&status, static_cast<const uint8_t*>(ws) + c.status, sizeof(status),
+                                    hipMemcpyDeviceToHost, s);
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    if (err != hipSuccess) return hip_fail(err);
+    return status == 0 ? MOE_OK : MOE_ETIMEOUT;
+}
+
 const char* moe_error_string(int code) {
     switch (code) {
         case MOE_OK: return "success";
         case MOE_EINVAL: return "invalid argument";
         case MOE_EUNSUPPORTED: return "unsupported shape";
         case MOE_EWORKSPACE: return "workspace too small or misaligned";
+        case MOE_ETIMEOUT: return "a bounded wait inside the last call gave up (its output is invalid)";
         case MOE_EHIP: return g_hip_error.empty() ? "HIP error" : g_hip_error.c_str();
         default: return "unknown error";
     }

@@ -66,12 +66,13 @@
 #include "common.h"
 #include "kernels.h"
 #include "mfma.h"
+#define MOE_HD __host__ __device__ __forceinline__
+#include "sched.h"
 
 namespace moe {
 
 constexpr int BK = kKStep;              // K per MFMA step (bytes of FP8 A per row)
-constexpr int kGM = 8;                  // m-tiles per tile-order group
-constexpr int kXCDs = 8;                // XCDs of the chip, dealt workgroups round-robin
+using sched::grouped_order;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -202,7 +203,7 @@ struct TileEngine {
     float* s_w;         // [2][BM] topk weight of the A row, GEMM1
     int* s_pair;        // [BM]    pair index of the A row, staging for the next tile
     int K, nk;          // reduction length and K steps
-    int64_t sa_slab, sb_slab;
+    int64_t sa_slab, sb_ks, sb_rs;     // activation scales per K step; weight scales per K step, row
     const uint8_t* a_base;
     const uint8_t* sa_base;
     // sources of the next K step to load (A, B, A scales, B scales), advanced
@@ -259,7 +260,8 @@ struct TileEngine {
         // step for row r sit at slab[ks][r][0..3], so a tile's scales for one K
         // step are 4-byte entries of one slab rather than bytes strided across rows.
         sa_slab = 4 * (kG1 ? p.T : p.T * p.topk);
-        sb_slab = 4 * (int64_t)(kG1 ? 2 * p.I : p.H);
+        sb_ks = kG1 ? p.w13sf_ks : p.w2sf_ks;
+        sb_rs = kG1 ? p.w13sf_rs : p.w2sf_rs;
         a_base = kG1 ? p.xq : p.hq;
         sa_base = kG1 ? p.xsf : p.hsf;
         const Lane L;
@@ -326,7 +328,7 @@ struct TileEngine {
             if (kG1) {
                 int icol = ntile * (BN / 2) + ws * (C::WTN / 2) + c * (C::NT / 2) + (nt >> 1);
                 icol = min(icol, p.I - 1);          // partial last n-tile: never stored
-                return (nt & 1) ? p.I + icol : icol;
+                return (uint32_t)w13_row(icol, nt & 1, p.I, p.w13_il);
             } else {
                 const int n = ntile * BN + ws * C::WTN + c * C::NT + nt;
                 return min(n, p.H - 1);
@@ -336,7 +338,7 @@ struct TileEngine {
         ld_a = a_base;
         ld_w = kG1 ? p.w13 + (int64_t)e * (2 * p.I) * b_stride : p.w2 + (int64_t)e * p.H * b_stride;
         ld_sa = sa_base;
-        ld_sw = (kG1 ? p.w13sf : p.w2sf) + (int64_t)e * nk * sb_slab;
+        ld_sw = (kG1 ? p.w13sf : p.w2sf) + (int64_t)e * (kG1 ? 2 * p.I : p.H) * (K / kGroup);
         // per-lane global sources of each load instruction (fixed over K), as
         // 32-bit byte offsets from wave-uniform bases
 #pragma unroll
@@ -358,7 +360,7 @@ struct TileEngine {
         // scale_slot_row: the slots of LDS row q hold weight row b_row(q).
 #pragma unroll
         for (int j = 0; j < C::kSBE; ++j)
-            sb_src[j] = b_row(scale_slot_row(64 * (C::kSBE * ew + j) + L.lane)) * 4u;
+            sb_src[j] = b_row(scale_slot_row(64 * (C::kSBE * ew + j) + L.lane)) * (uint32_t)sb_rs;
     }
 
     __device__ __forceinline__ uint8_t* stage_ptr(int stage) const { return smem + stage * C::kStage; }
@@ -391,7 +393,7 @@ struct TileEngine {
         ld_a += BK;
         ld_w += BK / 2;
         ld_sa += sa_slab;
-        ld_sw += sb_slab;
+        ld_sw += sb_ks;
     }
 
     // Rows of the tile in the K loop: a wave whose WTM rows all lie past the
@@ -637,21 +639,7 @@ MOE_DEV int gemm_ntiles(const GemmParams& p, bool g1) {
 }
 
 // Workgroup slot of this workgroup: consecutive for the workgroups of one XCD.
-MOE_DEV int xcd_slot() {
-    const int grid = gridDim.x;
-    return (grid % kXCDs) == 0 ? (blockIdx.x % kXCDs) * (grid / kXCDs) + blockIdx.x / kXCDs
-                               : blockIdx.x;
-}
-
-// Tile number t of a run of m-tiles [m0, m0 + nm) x nt n-tiles in the grouped
-// order: groups of kGM m-tiles x all n-tiles, m fastest inside a group.
-MOE_DEV void grouped_order(int t, int m0, int nm, int nt, int* mt, int* ntile) {
-    const int grp = t / (kGM * nt);
-    const int gm = min(kGM, nm - grp * kGM);
-    const int in_grp = t - grp * (kGM * nt);
-    *ntile = in_grp / gm;
-    *mt = m0 + grp * kGM + (in_grp - *ntile * gm);
-}
+MOE_DEV int xcd_slot() { return sched::tile_slot(blockIdx.x, gridDim.x); }
 
 // GEMM1 or GEMM2 alone (one launch each, ordered by the stream).  The K
 // pipeline of a workgroup runs on across its tiles: while a tile is in its K
@@ -740,30 +728,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams 
     const int NT1 = gemm_ntiles<BN>(p, true), NT2 = gemm_ntiles<BN>(p, false);
     const int ew = p.wave_experts;
     const int nw = (p.E + ew - 1) / ew;
-    const int nseg = 2 * nw;
-    // segment s of the list: GEMM1 of wave w = (s + 1) / 2 (s = 0 or odd),
-    // GEMM2 of wave w = s / 2 - 1 (s even > 0) and of the last wave (s = nseg - 1)
-    auto seg_of = [&](int sidx, int* g1, int* m0, int* nm) {
-        int w;
-        if (sidx == nseg - 1) { *g1 = 0; w = nw - 1; }
-        else if (sidx == 0 || (sidx & 1)) { *g1 = 1; w = (sidx + 1) / 2; }
-        else { *g1 = 0; w = sidx / 2 - 1; }
-        const int a = p.mtile_off[min(w * ew, p.E)], b = p.mtile_off[min((w + 1) * ew, p.E)];
-        *m0 = a;
-        *nm = b - a;
-    };
-    int seg = -1, seg_start = 0, seg_len = 0, g1 = 1, m0 = 0, nm = 0;
+    const int spin_limit = p.spin_limit > 0 ? p.spin_limit : kSpinLimit;
+    sched::FusedCursor cur;
     const int total = p.mtile_off[p.E] * (NT1 + NT2);
     for (int tile = xcd_slot(); tile < total; tile += gridDim.x) {
-        while (tile >= seg_start + seg_len) {      // advance to the segment holding tile
-            seg_start += seg_len;
-            ++seg;
-            seg_of(seg, &g1, &m0, &nm);
-            seg_len = nm * (g1 ? NT1 : NT2);
-        }
+        cur.seek(tile, nw, ew, p.E, p.mtile_off, NT1, NT2);
         int mt, ntile;
-        grouped_order(tile - seg_start, m0, nm, g1 ? NT1 : NT2, &mt, &ntile);
-        if (g1) {
+        cur.tile(tile, NT1, NT2, &mt, &ntile);
+        if (cur.sg.g1) {
             gemm_tile<BM, BN, WM, WN, true, true>(p, mt, ntile, smem);
             // every thread's coherent h stores have completed (vmcnt(0)) before the barrier
             __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8) | (0 << 14));
@@ -776,7 +748,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams 
                 while (__hip_atomic_load(p.ready + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                        NT1) {
                     __builtin_amdgcn_s_sleep(1);
-                    if (++n > kSpinLimit) {
+                    if (++n >= spin_limit) {
                         __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;
                     }
@@ -842,14 +814,8 @@ hipError_t launch_fused_gemm(const GemmParams& p_in, hipStream_t s, hipEvent_t e
     if (err != hipSuccess) return err;
     if (cus <= 0) return hipErrorInvalidDevice;
     GemmParams p = p_in;
-    // experts per wave: enough GEMM1 tiles to give every CU about two
-    // ("MegaMoE" notes, "Wave": ceil(2 * SMs / L1 blocks per expert))
-    const int64_t R = p.T * p.topk;
     const int nt1 = (p.I + kBN / 2 - 1) / (kBN / 2), nt2 = (p.H + kBN - 1) / kBN;
-    const int64_t rows_per_expert = std::max<int64_t>(1, (R + p.E - 1) / p.E);
-    const int64_t tiles_per_expert = (rows_per_expert + kBM - 1) / kBM * nt1;
-    p.wave_experts = (int)std::min<int64_t>(
-        p.E, std::max<int64_t>(1, (2 * (int64_t)cus + tiles_per_expert - 1) / tiles_per_expert));
+    p.wave_experts = sched::fused_wave_experts(p.T * p.topk, p.E, nt1, cus, kBM);
     // one workgroup per CU, all resident at once: a GEMM2 tile may wait for a GEMM1
     // tile of any other workgroup
     const int64_t upper = (int64_t)p.max_mtiles * (nt1 + nt2);

@@ -93,6 +93,13 @@ struct GemmParams {
                                 // whose h is stored
     int* status;                // [1] set to 1 if a wait gave up (never in a correct run)
     int wave_experts;           // experts per scheduling wave (set by the launcher)
+    int spin_limit;             // polls of a ready counter before a wait gives up; 0: the
+                                // kernel's own bound (about 0.5 s)
+    int w13_il;                 // W13 rows pre-interleaved: 8 gate rows, then the same 8
+                                // columns' up rows (else all gate rows, then all up rows)
+    // byte strides of the weight scales per weight row and per 128-wide K step:
+    // K-step major (4, 4 * rows) or per row (K / 32, 4)
+    int64_t w13sf_rs, w13sf_ks, w2sf_rs, w2sf_ks;
 };
 
 int gemm_bm();                  // rows per m-tile of the grouped GEMMs

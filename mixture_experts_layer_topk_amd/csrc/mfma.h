@@ -1,7 +1,9 @@
 // Arithmetic shared by the two grouped-GEMM kernels (the tiled one for many
-// rows per expert and the narrow one for few).  Both feed every output element
-// through the same sequence of scaled MFMAs, one per 128-wide K step in
-// increasing K order, and the same epilogue, so the two give identical bits.
+// rows per expert and the narrow one for few): the same per-step scaled MFMA
+// and the same epilogue arithmetic.  The tiled kernel accumulates every K step
+// into one accumulator chain in increasing K order; the narrow kernel splits K
+// into four ranges, one per wave, and adds the four partial sums in LDS, so the
+// two agree within the FP32 summation-order tolerance, not bit for bit.
 #pragma once
 
 #include "common.h"
@@ -23,6 +25,15 @@ MOE_DEV v4f mfma_fp8_fp4(const v8i& a, const v4i& b, const v4f& c, int sa, int s
 MOE_DEV float silu(float g) {
     const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
     return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Weight row of W13 that holds projection `up` (0: gate, 1: up) of I column
+// icol.  Canonical layout: all gate rows, then all up rows ("MegaMoE" study
+// notes, "原始权重布局").  Pre-interleaved (il != 0): groups of 8 gate rows, each
+// followed by the up rows of the same 8 columns (the same page's gran = 8
+// interleave).
+MOE_DEV int w13_row(int icol, int up, int I, int il) {
+    return il ? ((icol >> 3) << 4) + (up << 3) + (icol & 7) : up * I + icol;
 }
 
 // GEMM1 epilogue value of one element: silu(gate) * up * routing weight.

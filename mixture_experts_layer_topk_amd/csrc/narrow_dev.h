@@ -70,7 +70,10 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
     const uint8_t* aq = kG1 ? p.xq : p.hq;
     const uint8_t* asf = kG1 ? p.xsf : p.hsf;
     const int64_t a_slab = 4 * (kG1 ? p.T : R);          // bytes per K step of activation scales
-    const int64_t w_slab = 4 * wrows;                    // bytes per K step of weight scales
+    // weight-scale byte strides per weight row and per K step (layout-dependent)
+    const int64_t w_rs = kG1 ? p.w13sf_rs : p.w2sf_rs;
+    const int64_t w_ks = kG1 ? p.w13sf_ks : p.w2sf_ks;
+    const int spin_limit = p.spin_limit > 0 ? p.spin_limit : kNarrowSpinLimit;
     // this wave's K range; every wave runs nchunk items per unit
     const int kb = wave * nk / kNarrowWaves, ke = (wave + 1) * nk / kNarrowWaves;
     const int kr = (nk + kNarrowWaves - 1) / kNarrowWaves;
@@ -80,7 +83,7 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
     auto brow = [&](int nc, int t) -> int {
         if (kG1) {
             const int icol = nc * Cfg::kCols + (t & 1) * 16 + l16;
-            return (t >> 1) ? p.I + icol : icol;         // tiles 0, 1 gate; 2, 3 up
+            return w13_row(icol, t >> 1, p.I, p.w13_il);  // tiles 0, 1 gate; 2, 3 up
         }
         return nc * Cfg::kCols + 16 * t + l16;
     };
@@ -100,7 +103,7 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
             q = min(q, nitems - 1);
             const int c = q % nchunk;
             const uint8_t* wq_e = wq + (int64_t)e * wrows * (K / 2) + lg * 16;
-            const uint8_t* wsf_e = wsf + (int64_t)e * nk * w_slab;
+            const uint8_t* wsf_e = wsf + (int64_t)e * wrows * (K / kGroup);
 #pragma unroll
             for (int jj = 0; jj < KC; ++jj) {
                 const int ks = max(0, min(kb + c * KC + jj, min(ke, nk) - 1));
@@ -109,7 +112,7 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
                     const int br = brow(nc, t);
                     bf.b[jj][t] = *reinterpret_cast<const v4i*>(wq_e + (int64_t)br * (K / 2) +
                                                                 ks * (kKStep / 2));
-                    bf.sb[jj][t] = *reinterpret_cast<const uint32_t*>(wsf_e + ks * w_slab + br * 4);
+                    bf.sb[jj][t] = *reinterpret_cast<const uint32_t*>(wsf_e + ks * w_ks + br * w_rs);
                 }
             }
         };
@@ -194,7 +197,7 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
                     int n = 0;
                     while (__hip_atomic_load(p.ready + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
                         __builtin_amdgcn_s_sleep(1);
-                        if (++n > kNarrowSpinLimit) {
+                        if (++n >= spin_limit) {
                             __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                             break;
                         }

@@ -5,13 +5,27 @@ checks of the layer.
 Tolerances (floating point only; integer outputs are compared exactly):
   y     max|y - y_ref| <= 2e-2 * max|y_ref| and
         sum|y - y_ref| / sum|y_ref| <= 5e-3 (normalised L1 error)
-  hq    at most 0.1 % of the E4M3 intermediates differ, each by at most one
-        E4M3 step at the larger of the two values, or by at most 2^-12 of its
-        group's range 448 * scale (FP32 accumulation order and the exp of SiLU
-        may move a value across a rounding boundary; the FP32 accumulation
-        error of a dot product scales with the sum of |products|, so values
-        that are small through cancellation can move by a few codes)
+  hq    the E4M3 intermediates, compared as values (code x scale):
+          - at most 0.1 % of them differ;
+          - a differing value is at most one E4M3 grid step from the reference,
+            measured on the grid of the larger of the two group scales;
+          - the only exception is a value whose own rounding error bound
+            allows more: the GPU and the reference each round a dot product of
+            K FP8 x FP4 products in FP32, in different orders, so each
+            accumulator (gate g, up u) may differ by gamma_K * sum_k |a_k b_k|
+            (Higham's bound, gamma_K = K u / (1 - K u), u = 2^-24), which
+            reaches h = silu(g) * u * w through |w| (L dg (|u| + du) +
+            |silu(g)| du) with L = max |silu'| < 1.1, plus a few FP32 roundings
+            of silu and the products; the two values may then differ by that
+            bound plus one grid step.  Values that are small through
+            cancellation (|h| far below sum_k |a_k b_k|) are the only ones it
+            lets move by more than a step; at most 1e-4 of the values may use
+            it, and each is reported.
   topk_w  relative 4e-6 (float32 exp/divide against the float64 reference)
+
+Every check prints its margins (the y error ratios against their limits, the
+fraction of differing hq values, the largest distance in grid steps and the
+number of values beyond one step).
 """
 from __future__ import annotations
 
@@ -45,12 +59,27 @@ def bf16_dev(bits: np.ndarray):
     return to_dev(bits.view(np.int16), torch.bfloat16)
 
 
-@functools.lru_cache(maxsize=64)
-def oracle_expert(w: W.Workload, e: int):
-    """Oracle-packed weights of expert e (from the same seeded BF16 values)."""
+@functools.lru_cache(maxsize=320)
+def _oracle_expert(seed: int, H: int, I: int, e: int):
+    w = W.Workload("weights", T=1, H=H, I=I, E=e + 1, topk=1, seed=seed)
     q13, s13 = M.pack_weights(W.gen_expert_w13(w, e))
     q2, s2 = M.pack_weights(W.gen_expert_w2(w, e))
     return q13, s13, q2, s2
+
+
+def oracle_expert(w: W.Workload, e: int):
+    """Oracle-packed weights of expert e (from the same seeded BF16 values; the
+    weights depend on the seed and shapes only, so workloads that differ in their
+    tokens or routing share them)."""
+    return _oracle_expert(w.seed, w.H, w.I, int(e))
+
+
+def prefetch_oracle_experts(w: W.Workload, experts=None, threads: int = 16):
+    """Pack the listed experts' weights with the oracle on a thread pool (numpy
+    releases the GIL in the heavy steps), so later serial lookups hit the cache."""
+    experts = range(w.E) if experts is None else experts
+    with ThreadPoolExecutor(min(threads, os.cpu_count() or 1)) as ex:
+        list(ex.map(lambda e: oracle_expert(w, e), experts))
 
 
 class LazyExperts:
@@ -122,7 +151,7 @@ def y_bits(y: torch.Tensor) -> np.ndarray:
     return y.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def check_y(y_gpu_bits, y_ref_bits, rows=None):
+def check_y(y_gpu_bits, y_ref_bits, rows=None, label="y"):
     a = C.bf16_value(y_gpu_bits).astype(np.float64)
     b = C.bf16_value(y_ref_bits).astype(np.float64)
     if rows is not None:
@@ -131,38 +160,97 @@ def check_y(y_gpu_bits, y_ref_bits, rows=None):
     err = np.abs(a - b)
     mx = np.abs(b).max()
     l1 = err.sum() / max(np.abs(b).sum(), 1e-30)
+    print(f"    {label}: {a.shape[0]} rows, max|dy|/max|y| = {err.max() / mx:.3e} (limit 2e-2), "
+          f"normalised L1 = {l1:.3e} (limit 5e-3)", flush=True)
     assert err.max() <= 2e-2 * mx, f"max err {err.max()} vs {2e-2 * mx}"
     assert l1 <= 5e-3, f"normalised L1 {l1}"
     return err.max() / mx, l1
 
 
-def e4m3_step(v: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """One E4M3 grid step at value |v| for scale s (subnormal step below 2^-6 s)."""
-    mag = np.abs(v) / s
-    ex = np.floor(np.log2(np.maximum(mag, 2.0 ** -6)))
-    return np.ldexp(1.0, (ex - 3).astype(int)) * s
+def e4m3_position(v: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Signed position of value v on the E4M3 grid of scale s, in grid steps from
+    zero: the code's magnitude index (8 * biased exponent + mantissa, 0..126) for
+    grid values, linear in between.  Positions of two values of one grid differ by
+    the number of grid steps between them."""
+    x = np.abs(v) / s
+    sub = x < 2.0 ** -6
+    ex = np.floor(np.log2(np.where(sub, 1.0, x)))
+    pos = np.where(sub, x * 2.0 ** 9, 8.0 * (ex + 7) + (x / np.ldexp(1.0, ex.astype(int)) - 1.0) * 8.0)
+    return np.sign(v) * pos
 
 
-def check_hq(hq_g, hsf_g, hq_r, hsf_r, max_frac=1e-3):
+def check_hq(hq_g, hsf_g, hq_r, hsf_r, max_frac=1e-3, bound=None, max_beyond=1e-4, label="hq"):
+    """hq against the reference (see the module docstring).  bound(rows, cols)
+    returns the accumulation-order bound of |h_gpu - h_ref| for those elements
+    (float64); without it no value may be more than one grid step away."""
     a = C.dequantize_blocks(hq_g, hsf_g, "e4m3")
     b = C.dequantize_blocks(hq_r, hsf_r, "e4m3")
     diff = a != b
-    frac = diff.mean() if diff.size else 0.0
-    assert frac <= max_frac, f"{frac:.2e} of hq differ"
-    if diff.any():
+    n = diff.size
+    nd = int(diff.sum())
+    frac = nd / n if n else 0.0
+    max_steps, beyond = 0.0, 0
+    if nd:
         s = np.maximum(np.repeat(C.e8m0_value(hsf_g), 32, -1), np.repeat(C.e8m0_value(hsf_r), 32, -1))
-        big = np.maximum(np.abs(a), np.abs(b))
-        step = e4m3_step(big, s)
-        tol = np.maximum(step, 448.0 * s * 2.0 ** -12)
-        bad = diff & (np.abs(a - b) > tol * (1 + 1e-12))
-        if bad.any():
-            r, c = np.nonzero(bad)
+        r, c = np.nonzero(diff)
+        sd = s[r, c]
+        steps = np.abs(e4m3_position(a[r, c], sd) - e4m3_position(b[r, c], sd))
+        max_steps = float(steps.max())
+        far = steps > 1.0 + 1e-9
+        beyond = int(far.sum())
+        if beyond:
+            rr, cc = r[far], c[far]
+            big = np.maximum(np.abs(a[rr, cc]), np.abs(b[rr, cc]))
+            pos = e4m3_position(big, sd[far])
+            # one grid step at the larger value: 2^-9 s below 2^-6 s, else 2^(e-3) s
+            step = np.where(pos < 8.0, 2.0 ** -9, np.ldexp(1.0, (np.floor(pos / 8.0) - 7 - 3).astype(int))) * sd[far]
+            if bound is None:
+                lim = np.zeros_like(step)
+            else:
+                lim = bound(rr, cc)
+            bad = np.abs(a[rr, cc] - b[rr, cc]) > (lim + step) * (1 + 1e-9)
             lines = [f"row {i} col {j}: gpu code {hq_g[i, j]:#04x} sf {hsf_g[i, j // 32]} = {a[i, j]:.6g}, "
-                     f"ref code {hq_r[i, j]:#04x} sf {hsf_r[i, j // 32]} = {b[i, j]:.6g}"
-                     for i, j in list(zip(r, c))[:12]]
-            raise AssertionError(f"{bad.sum()} hq values differ beyond tolerance "
-                                 f"(rows {np.unique(r)[:20]}):\n" + "\n".join(lines))
+                     f"ref code {hq_r[i, j]:#04x} sf {hsf_r[i, j // 32]} = {b[i, j]:.6g}, "
+                     f"bound {l:.3g} + step {st:.3g}"
+                     for i, j, l, st in list(zip(rr, cc, lim, step))[:12]]
+            print(f"    {label}: {beyond} value(s) beyond one grid step:\n      " + "\n      ".join(lines),
+                  flush=True)
+            assert not bad.any(), f"{int(bad.sum())} hq values differ beyond their accumulation bound"
+    print(f"    {label}: {n} values, {nd} differ ({frac:.2e}, limit {max_frac:.0e}); largest distance "
+          f"{max_steps:.3g} grid steps; {beyond} beyond one step (limit {max_beyond:.0e} of the values)",
+          flush=True)
+    assert frac <= max_frac, f"{frac:.2e} of hq differ"
+    assert beyond <= max_beyond * n, f"{beyond} hq values beyond one grid step"
     return frac
+
+
+def make_hq_bound(ref, pairs, w13q, w13sf, topk: int, I: int):
+    """bound(rows, cols) for check_hq: compared row i is pair pairs[i] = t*topk + j of
+    the reference ``ref`` (an oracle forward); w13q/w13sf index the oracle's packed
+    weights by expert.  Recomputes g, u and sum_k |a_k b_k| of each asked element in
+    float64 from the dequantised operands."""
+    u32 = 2.0 ** -24
+
+    def bound(rows, cols):
+        out = np.empty(len(rows))
+        for n, (i, c) in enumerate(zip(rows, cols)):
+            f = int(pairs[i])
+            t, j = f // topk, f % topk
+            e = int(ref["topk_idx"][t, j])
+            wt = float(ref["topk_w"][t, j])
+            a = C.dequantize_blocks(ref["xq"][t:t + 1], ref["xsf"][t:t + 1], "e4m3")[0]
+            K = a.size
+            rows13 = C.dequantize_blocks(C.unpack_e2m1(w13q[e][[c, I + c]]), w13sf[e][[c, I + c]], "e2m1")
+            g, u = float(a @ rows13[0]), float(a @ rows13[1])
+            gamma = (K + 1) * u32 / (1 - (K + 1) * u32)
+            dg = gamma * float(np.abs(a) @ np.abs(rows13[0]))
+            du = gamma * float(np.abs(a) @ np.abs(rows13[1]))
+            silu = g / (1.0 + np.exp(-g)) if g > -700 else 0.0
+            h = silu * u * wt
+            out[n] = abs(wt) * (1.1 * dg * (abs(u) + du) + (abs(silu) + 1.1 * dg) * du) + 16 * u32 * abs(h)
+        return out
+
+    return bound
 
 
 def check_bucketize(inter, idx_ref, E):

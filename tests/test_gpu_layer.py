@@ -145,6 +145,26 @@ def test_route_ties_bit_exact(T, E, topk):
 
 # ------------------------------------------------------------------ whole layer
 
+def _pairs_of(w, tokens=None):
+    if tokens is None:
+        return np.arange(w.T * w.topk)
+    return (np.asarray(tokens)[:, None] * w.topk + np.arange(w.topk)[None, :]).reshape(-1)
+
+
+def _check_layer(inter, y, ref, w, label, tokens=None):
+    """hq of every compared (token, slot) pair, matched through slot_of on each side,
+    and y of every compared token, against the oracle (tolerances in gpu_common)."""
+    so_g = inter["slot_of"].reshape(-1)
+    so_r = ref["slot_of"].reshape(-1)
+    pairs = _pairs_of(w, tokens)
+    pairs = pairs[so_r[pairs] >= 0]                 # masked slots have no row
+    wq = G.oracle_weights(w)
+    bound = G.make_hq_bound(ref, pairs, wq[0], wq[1], w.topk, w.I)
+    G.check_hq(inter["hq"][so_g[pairs]], inter["hsf"][so_g[pairs]], ref["hq"][so_r[pairs]],
+               ref["hsf"][so_r[pairs]], bound=bound, label=f"{label} hq")
+    G.check_y(G.y_bits(y), ref["y"], rows=tokens, label=f"{label} y")
+
+
 @pytest.mark.parametrize("w", SMALL_SHAPES, ids=lambda w: w.name)
 def test_forward_matches_oracle(w):
     _log(f"forward {w.name}")
@@ -156,11 +176,7 @@ def test_forward_matches_oracle(w):
     G.check_bucketize(inter, ref["topk_idx"], w.E)
     assert np.array_equal(inter["xq"], ref["xq"])
     assert np.array_equal(inter["xsf"], ref["xsf"])
-    # hq by (t, j): map GPU positions and oracle positions through slot_of
-    so_g = inter["slot_of"].reshape(-1)
-    so_r = ref["slot_of"].reshape(-1)
-    G.check_hq(inter["hq"][so_g], inter["hsf"][so_g], ref["hq"][so_r], ref["hsf"][so_r])
-    G.check_y(G.y_bits(y), ref["y"])
+    _check_layer(inter, y, ref, w, w.name)
 
 
 def test_forward_decode_matches_oracle():
@@ -169,34 +185,221 @@ def test_forward_decode_matches_oracle():
     dl = G.DeviceLayer(w)
     y = dl.forward()
     ref = _oracle_full(w)
-    inter = dl.intermediates()
-    so_g, so_r = inter["slot_of"].reshape(-1), ref["slot_of"].reshape(-1)
-    G.check_hq(inter["hq"][so_g], inter["hsf"][so_g], ref["hq"][so_r], ref["hsf"][so_r])
-    G.check_y(G.y_bits(y), ref["y"])
+    _check_layer(dl.intermediates(), y, ref, w, "decode")
 
 
-@pytest.mark.parametrize("name", ["dsv3_prefill", "dsv3_skewed", "full256"])
-def test_forward_full_size_sampled_tokens(name):
-    """Full-size launch; the oracle recomputes a sample of tokens one by one (only
-    the experts those tokens touch are generated and quantised on its side)."""
+# Full-size workloads: the device layer and the oracle's result are built once per
+# workload and shared by the tests that use them.
+_BIG = {}
+
+
+def _big(name, tokens=None):
+    key = (name, None if tokens is None else tuple(tokens))
+    if key not in _BIG:
+        w = W.WORKLOADS[name]
+        dl = _BIG.get((name, "layer")) or G.DeviceLayer(w)
+        _BIG[(name, "layer")] = dl
+        experts = None
+        if tokens is not None:
+            idx, _ = M.route(dl.logits_np, w.topk, w.score_fn, bool(w.renorm))
+            experts = np.unique(idx[np.asarray(tokens)])
+        G.prefetch_oracle_experts(w, experts)
+        _BIG[key] = M.forward(dl.x_np, *G.oracle_weights(w), topk=w.topk, I=w.I, logits=dl.logits_np,
+                              score_fn=w.score_fn, renorm=bool(w.renorm), tokens=tokens, workers=16)
+    return _BIG[(name, "layer")], _BIG[key]
+
+
+@pytest.mark.parametrize("name", ["dsv3_prefill", "dsv3_skewed"])
+def test_forward_full_size_every_token(name):
+    """The DeepSeek-V3-like shapes in full: every token's y and every pair's hq
+    (the whole 56-step K loop, every m-tile of every expert, the skewed workload's
+    hot and near-empty experts) against the oracle on all tokens."""
     w = W.WORKLOADS[name]
-    _log(f"forward {name} (sampled)")
-    dl = G.DeviceLayer(w)
+    _log(f"forward {name} (every token)")
+    dl, ref = _big(name)
     y = dl.forward()
     inter = dl.intermediates()
-    logits = dl.logits_np
-    idx, _ = M.route(logits, w.topk, w.score_fn, bool(w.renorm))
-    assert np.array_equal(inter["topk_idx"], idx)
-    G.check_bucketize(inter, idx, w.E)
-    toks = [0, w.T // 3, 2 * w.T // 3, w.T - 1]
-    ref = M.forward(dl.x_np, *G.oracle_weights(w), topk=w.topk, I=w.I, logits=logits,
-                    score_fn=w.score_fn, renorm=bool(w.renorm), tokens=toks)
-    G.check_y(G.y_bits(y), ref["y"], rows=toks)
-    so_g = inter["slot_of"][toks].reshape(-1)
-    so_r = ref["slot_of"][toks].reshape(-1)
-    G.check_hq(inter["hq"][so_g], inter["hsf"][so_g], ref["hq"][so_r], ref["hsf"][so_r])
-    # every output row is finite and the untouched workspace regions stay consistent
-    assert torch.isfinite(y.float()).all()
+    assert np.array_equal(inter["topk_idx"], ref["topk_idx"])
+    G.check_bucketize(inter, ref["topk_idx"], w.E)
+    assert np.array_equal(inter["xq"], ref["xq"])
+    assert np.array_equal(inter["xsf"], ref["xsf"])
+    _check_layer(inter, y, ref, w, name)
+
+
+def _fused_waves(w):
+    """Expert waves of the one-launch list on this GPU (the launcher's formula)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nt1 = (w.I + 255) // 256
+    per_expert = max(1, -(-w.T * w.topk // w.E))
+    tiles = -(-per_expert // 128) * nt1
+    ew = min(w.E, max(1, -(-2 * cus // tiles)))
+    return -(-w.E // ew)
+
+
+def test_one_launch_full_size_dsv3_prefill():
+    """The one-launch scheduler at the DeepSeek-V3-like shape (4 expert waves on
+    256 CUs: GEMM1 of wave w + 1 runs between GEMM1 and GEMM2 of wave w), every
+    token against the oracle."""
+    m = G.lib()
+    w = W.WORKLOADS["dsv3_prefill"]
+    waves = _fused_waves(w)
+    _log(f"one launch dsv3_prefill (every token, {waves} expert waves)")
+    assert waves >= 2
+    dl, ref = _big("dsv3_prefill")
+    y = dl.forward(flags=m.FLAG_ONE_LAUNCH)
+    _check_layer(dl.intermediates(), y, ref, w, f"one launch, {waves} waves")
+
+
+def _full256_tokens(inter, w):
+    """One token in the last (ragged) 128-row m-tile of every expert, by the GPU's
+    own positions, plus a seeded sample of 64 tokens."""
+    off = inter["offsets"]
+    src = inter["slot_src"]
+    toks = set()
+    for e in range(w.E):
+        if off[e + 1] > off[e]:
+            toks.add(int(src[off[e + 1] - 1]) // w.topk)     # last row of the last m-tile
+    toks |= set(np.random.default_rng(1234).choice(w.T, 64, replace=False).tolist())
+    return sorted(toks)
+
+
+@pytest.mark.parametrize("flags", ["default", "one-launch"])
+def test_forward_full256_every_expert_tail(flags):
+    """256 experts on one GPU (8 expert waves in the one-launch list): y and hq of
+    tokens covering the last, ragged m-tile of every expert."""
+    m = G.lib()
+    w = W.WORKLOADS["full256"]
+    _log(f"forward full256 ({flags}; one token in every expert's last m-tile)")
+    dl = _BIG.get(("full256", "layer")) or G.DeviceLayer(w)
+    _BIG[("full256", "layer")] = dl
+    f = m.FLAG_ONE_LAUNCH if flags == "one-launch" else m.FLAG_NONE
+    y = dl.forward(flags=f)
+    inter = dl.intermediates()
+    counts = inter["counts"]
+    ragged = int(((counts % 128) != 0).sum())
+    toks = _full256_tokens(inter, w)
+    _log(f"  {len(toks)} tokens; {ragged} of {w.E} experts end in a partial m-tile; "
+         f"{_fused_waves(w)} expert waves")
+    dl2, ref = _big("full256", toks)
+    assert np.array_equal(inter["topk_idx"], ref["topk_idx"])
+    G.check_bucketize(inter, ref["topk_idx"], w.E)
+    _check_layer(inter, y, ref, w, f"full256 {flags}", tokens=toks)
+
+
+# Shapes whose one-launch list has several expert waves on 256 CUs (3072 rows per
+# expert on average: 24 m-tiles x 8 GEMM1 n-tiles, so 3 experts per wave), with
+# uniform and Zipf-skewed routing
+WAVE_SHAPES = [W.Workload("wave_uniform", T=3072, H=256, I=2048, E=8, topk=8),
+               W.Workload("wave_skewed", T=6144, H=256, I=2048, E=8, topk=4, zipf_s=1.2)]
+
+
+@pytest.mark.parametrize("w", WAVE_SHAPES, ids=lambda w: w.name)
+def test_one_launch_multi_wave(w):
+    m = G.lib()
+    waves = _fused_waves(w)
+    _log(f"one launch {w.name} ({waves} expert waves)")
+    assert waves >= 2, "the shape must give several expert waves"
+    dl = G.DeviceLayer(w)
+    ref = _oracle_full(w)
+    for name, flag in (("one launch", m.FLAG_ONE_LAUNCH), ("two launches", m.FLAG_TILED)):
+        y = dl.forward(flags=flag)
+        inter = dl.intermediates()
+        _log(f"  {name}: counts {inter['counts'].tolist()}")
+        _check_layer(inter, y, ref, w, f"{w.name} {name}")
+
+
+def test_workspace_poisoned_except_counters():
+    """After moe_workspace_init, every workspace byte past the counter header is set
+    to 0xFF: each path must write every region it reads (only the counters need the
+    one-time zeroing)."""
+    m = G.lib()
+    w = RAGGED
+    _log("poisoned workspace")
+    dl = G.DeviceLayer(w)
+    ref = _oracle_full(w)
+    status_off = m.workspace_layout(dl.d).status
+    for name, flag in (("default", m.FLAG_NONE), ("narrow", m.FLAG_NARROW), ("tiled", m.FLAG_TILED),
+                       ("one launch", m.FLAG_ONE_LAUNCH), ("narrow one launch", m.FLAG_NARROW | m.FLAG_ONE_LAUNCH)):
+        dl.ws[status_off:] = 0xFF
+        y = dl.forward(flags=flag)
+        _check_layer(dl.intermediates(), y, ref, w, f"poisoned, {name}")
+    wd = W.WORKLOADS["decode"]
+    dd = G.DeviceLayer(wd)
+    refd = _oracle_full(wd)
+    dd.ws[m.workspace_layout(dd.d).status:] = 0xFF
+    y = dd.forward(flags=m.FLAG_ONE_KERNEL)
+    _check_layer(dd.intermediates(), y, refd, wd, "poisoned, one kernel")
+
+
+@pytest.mark.parametrize("w", [RAGGED, W.WORKLOADS["decode"]], ids=lambda w: w.name)
+def test_weight_layout_flags(w):
+    """Pre-interleaved W13 (the pages' gran-8 gate/up interleave, built by the
+    oracle's interleave from the oracle-packed weights) and per-row weight scales
+    give the oracle's result on every GEMM path, bit-identical to the canonical
+    layout."""
+    m = G.lib()
+    _log(f"weight layout flags {w.name}")
+    dl = G.DeviceLayer(w)
+    ref = _oracle_full(w)
+    q13 = np.stack([G.oracle_expert(w, e)[0] for e in range(w.E)])
+    s13 = np.stack([G.oracle_expert(w, e)[1] for e in range(w.E)])
+    iq, isf = M.interleave_w13(q13, s13)
+    iq_d, isf_d = G.to_dev(iq), G.to_dev(isf)
+    isf_k = m.scales_kmajor(isf_d, w.H)
+    paths = [("narrow", m.FLAG_NARROW), ("tiled", m.FLAG_TILED), ("one launch", m.FLAG_ONE_LAUNCH),
+             ("narrow one launch", m.FLAG_NARROW | m.FLAG_ONE_LAUNCH)]
+    if w.T * w.topk <= 1024:
+        paths.append(("one kernel", m.FLAG_ONE_KERNEL))
+    for name, flag in paths:
+        base = G.y_bits(dl.forward(flags=flag))
+        variants = {
+            "interleaved": (iq_d, isf_k, dl.w2q, dl.w2sf_k, m.FLAG_W13_PREINTERLEAVED),
+            "per-row scales": (dl.w13q, dl.w13sf, dl.w2q, dl.w2sf, m.FLAG_W_SCALES_PER_ROW),
+            "both": (iq_d, isf_d, dl.w2q, dl.w2sf, m.FLAG_W13_PREINTERLEAVED | m.FLAG_W_SCALES_PER_ROW),
+        }
+        for vname, (a13, b13, a2, b2, vf) in variants.items():
+            y = m.forward(dl.d, dl.x, a13, b13, a2, b2, dl.ws, logits=dl.logits,
+                          flags=flag | vf | m.FLAG_KEEP_INTERMEDIATES)
+            torch.cuda.synchronize()
+            _check_layer(dl.intermediates(), y, ref, w, f"{name}, {vname}")
+            assert np.array_equal(G.y_bits(y), base), f"{name}, {vname}: y differs from the canonical layout"
+
+
+def test_check_status_reports_the_status_word():
+    """moe_check_status reads the status word a call leaves; a forward clears it."""
+    m = G.lib()
+    w = RAGGED
+    _log("check_status")
+    dl = G.DeviceLayer(w)
+    dl.forward()
+    assert m.check_status(dl.ws) == m.MOE_OK
+    status_off = m.workspace_layout(dl.d).status
+    dl.ws[status_off:status_off + 4] = torch.tensor([1, 0, 0, 0], dtype=torch.uint8, device="cuda")
+    assert m.check_status(dl.ws) == m.MOE_ETIMEOUT
+    dl.forward()
+    assert m.check_status(dl.ws) == m.MOE_OK
+
+
+@pytest.mark.parametrize("w", [WAVE_SHAPES[0], W.WORKLOADS["decode"]], ids=lambda w: w.name)
+def test_debug_spin_bound_ends_and_reports(w):
+    """With DEBUG_SPIN_BOUND every ready-counter wait of the one-launch paths gives
+    up after one failed poll: the call still ends, and moe_check_status agrees with
+    the status word; the next call without the flag is correct again."""
+    m = G.lib()
+    _log(f"debug spin bound {w.name}")
+    dl = G.DeviceLayer(w)
+    ref = _oracle_full(w)
+    base = m.FLAG_NARROW | m.FLAG_ONE_LAUNCH if w.name == "decode" else m.FLAG_ONE_LAUNCH
+    for _ in range(3):
+        m.forward(dl.d, dl.x, dl.w13q, dl.w13sf_k, dl.w2q, dl.w2sf_k, dl.ws, logits=dl.logits,
+                  flags=base | m.FLAG_DEBUG_SPIN_BOUND)
+        rc = m.check_status(dl.ws)
+        word = int(m.intermediates(dl.d, dl.ws)["status"].item())
+        _log(f"  status word {word}, check_status {rc}")
+        assert rc == (m.MOE_OK if word == 0 else m.MOE_ETIMEOUT)
+    y = dl.forward(flags=base)
+    assert m.check_status(dl.ws) == m.MOE_OK
+    _check_layer(dl.intermediates(), y, ref, w, f"{w.name} after debug spin bound")
 
 
 @pytest.mark.parametrize("path", ["narrow", "tiled"])
@@ -276,7 +479,6 @@ def test_narrow_and_tiled_gemms_match_oracle(w):
         ext = (np.full((w.T, 1), 3, np.int32), np.ones((w.T, 1), np.float32))
     dl = G.DeviceLayer(w, external_topk=ext)
     ref = _oracle_full(w, ext)
-    so_r = ref["slot_of"].reshape(-1)
     paths = [("narrow", m.FLAG_NARROW), ("narrow, one launch", m.FLAG_NARROW | m.FLAG_ONE_LAUNCH),
              ("tiled, two launches", m.FLAG_TILED), ("tiled, one launch", m.FLAG_ONE_LAUNCH)]
     if w.T * w.topk <= 1024:
@@ -284,12 +486,7 @@ def test_narrow_and_tiled_gemms_match_oracle(w):
     for name, flag in paths:
         _log(f"  {name}")
         y = dl.forward(use_logits=ext is None, flags=flag)
-        inter = dl.intermediates()
-        so_g = inter["slot_of"].reshape(-1)
-        ok = so_r >= 0
-        G.check_hq(inter["hq"][so_g[ok]], inter["hsf"][so_g[ok]], ref["hq"][so_r[ok]],
-                   ref["hsf"][so_r[ok]])
-        G.check_y(G.y_bits(y), ref["y"])
+        _check_layer(dl.intermediates(), y, ref, w, f"{w.name} {name}")
 
 
 # More tiles than workgroups, so that workgroups run several tiles back to back:
@@ -309,15 +506,11 @@ def test_tiled_gemms_many_tiles_per_workgroup(w):
     _log(f"many tiles per workgroup {w.name}")
     dl = G.DeviceLayer(w)
     ref = _oracle_full(w)
-    so_r = ref["slot_of"].reshape(-1)
     for name, flag in (("tiled, two launches", m.FLAG_TILED),
                        ("tiled, one launch", m.FLAG_ONE_LAUNCH)):
         _log(f"  {name}")
         y = dl.forward(flags=flag)
-        inter = dl.intermediates()
-        so_g = inter["slot_of"].reshape(-1)
-        G.check_hq(inter["hq"][so_g], inter["hsf"][so_g], ref["hq"][so_r], ref["hsf"][so_r])
-        G.check_y(G.y_bits(y), ref["y"])
+        _check_layer(dl.intermediates(), y, ref, w, f"{w.name} {name}")
 
 
 def test_one_launch_reads_this_calls_h():

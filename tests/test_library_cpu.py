@@ -73,7 +73,9 @@ def test_forward_rejects_null_and_small_workspace_without_gpu():
     a.x = fake
     for bad_flags in (m.FLAG_NARROW | m.FLAG_TILED, m.FLAG_NARROW | m.FLAG_TILED | m.FLAG_ONE_LAUNCH,
                       m.FLAG_ONE_KERNEL | m.FLAG_TILED, m.FLAG_ONE_KERNEL | m.FLAG_ONE_LAUNCH,
-                      16, 1 << 31):                                            # unknown or conflicting
+                      # the one-kernel layer's grid barriers guard the tables its phases index with
+                      m.FLAG_ONE_KERNEL | m.FLAG_DEBUG_SPIN_BOUND,
+                      256, 1 << 31):                                           # unknown or conflicting
         a.flags = bad_flags
         assert m._lib.moe_forward(ctypes.byref(a), None) == m.MOE_EINVAL
     # the one-kernel layer takes at most 1024 routed pairs
@@ -94,8 +96,15 @@ def test_quant_and_pack_reject_bad_sizes():
 
 def test_error_strings():
     m = _lib()
-    for code in (0, -1, -2, -3, -4, -99):
+    for code in (0, -1, -2, -3, -4, -5, -99):
         assert m._lib.moe_error_string(code)
+    assert b"wait" in m._lib.moe_error_string(m.MOE_ETIMEOUT)
+
+
+def test_check_status_rejects_bad_workspace_without_gpu():
+    m = _lib()
+    assert m._lib.moe_check_status(None, None) == m.MOE_EINVAL
+    assert m._lib.moe_check_status(ctypes.c_void_p((1 << 20) + 8), None) == m.MOE_EINVAL   # misaligned
 
 
 def test_ctypes_structs_match_the_c_header(tmp_path):
