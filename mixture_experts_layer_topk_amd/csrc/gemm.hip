@@ -192,7 +192,9 @@ MOE_DEV void load_lds4(const void* g, uint8_t* lds) {
 // other XCDs wrote in the same launch; h is then stored and read with
 // device-coherent accesses (sc1), which go to the memory-side cache instead of
 // an XCD's own L2, while the weights keep the cached path.
-template <int BM, int BN, int WM, int WN, bool kG1, bool kCoh>
+// kIL: W13 is in the gran-8 gate/up row interleave (a compile-time choice: a
+// run-time select in the row mapping costs the GEMM1 kernel register spills).
+template <int BM, int BN, int WM, int WN, bool kG1, bool kCoh, bool kIL = false>
 struct TileEngine {
     using C = Cfg<BM, BN, WM, WN, kG1>;
     static constexpr int kAuxA = (kCoh && !kG1) ? kCohAux : 0;
@@ -203,7 +205,7 @@ struct TileEngine {
     float* s_w;         // [2][BM] topk weight of the A row, GEMM1
     int* s_pair;        // [BM]    pair index of the A row, staging for the next tile
     int K, nk;          // reduction length and K steps
-    int64_t sa_slab, sb_ks, sb_rs;     // activation scales per K step; weight scales per K step, row
+    int64_t sa_slab, sb_ks;     // bytes per K step of the activation and the weight scales
     const uint8_t* a_base;
     const uint8_t* sa_base;
     // sources of the next K step to load (A, B, A scales, B scales), advanced
@@ -261,7 +263,6 @@ struct TileEngine {
         // step are 4-byte entries of one slab rather than bytes strided across rows.
         sa_slab = 4 * (kG1 ? p.T : p.T * p.topk);
         sb_ks = kG1 ? p.w13sf_ks : p.w2sf_ks;
-        sb_rs = kG1 ? p.w13sf_rs : p.w2sf_rs;
         a_base = kG1 ? p.xq : p.hq;
         sa_base = kG1 ? p.xsf : p.hsf;
         const Lane L;
@@ -328,7 +329,7 @@ struct TileEngine {
             if (kG1) {
                 int icol = ntile * (BN / 2) + ws * (C::WTN / 2) + c * (C::NT / 2) + (nt >> 1);
                 icol = min(icol, p.I - 1);          // partial last n-tile: never stored
-                return (uint32_t)w13_row(icol, nt & 1, p.I, p.w13_il);
+                return (uint32_t)w13_row(icol, nt & 1, p.I, kIL);
             } else {
                 const int n = ntile * BN + ws * C::WTN + c * C::NT + nt;
                 return min(n, p.H - 1);
@@ -360,7 +361,8 @@ struct TileEngine {
         // scale_slot_row: the slots of LDS row q hold weight row b_row(q).
 #pragma unroll
         for (int j = 0; j < C::kSBE; ++j)
-            sb_src[j] = b_row(scale_slot_row(64 * (C::kSBE * ew + j) + L.lane)) * (uint32_t)sb_rs;
+            sb_src[j] = b_row(scale_slot_row(64 * (C::kSBE * ew + j) + L.lane)) *
+                        (uint32_t)(kG1 ? p.w13sf_rs : p.w2sf_rs);
     }
 
     __device__ __forceinline__ uint8_t* stage_ptr(int stage) const { return smem + stage * C::kStage; }
@@ -607,9 +609,9 @@ struct TileEngine {
 };
 
 // One tile, loaded, computed and stored on its own (the one-launch kernel).
-template <int BM, int BN, int WM, int WN, bool kG1, bool kCoh>
+template <int BM, int BN, int WM, int WN, bool kG1, bool kCoh, bool kIL>
 MOE_DEV void gemm_tile(const GemmParams& p, int mt, int ntile, uint8_t* smem) {
-    TileEngine<BM, BN, WM, WN, kG1, kCoh> eng(p, smem);
+    TileEngine<BM, BN, WM, WN, kG1, kCoh, kIL> eng(p, smem);
     const int4 rec = p.mtile_rec[mt];        // {expert, first position, rows}
     eng.load_rows_now(rec, 0);
     eng.set_tile(rec, ntile, 0);
@@ -647,10 +649,10 @@ MOE_DEV int xcd_slot() { return sched::tile_slot(blockIdx.x, gridDim.x); }
 // sources set up (step nk - 2), and the last two steps issue the next tile's
 // first two K steps instead of reloading the current tile's last one, so the
 // epilogue overlaps those loads and the next tile starts on a full pipeline.
-template <int BM, int BN, int WM, int WN, bool kG1>
+template <int BM, int BN, int WM, int WN, bool kG1, bool kIL>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    using Eng = TileEngine<BM, BN, WM, WN, kG1, false>;
+    using Eng = TileEngine<BM, BN, WM, WN, kG1, false, kIL>;
     const int NT = gemm_ntiles<BN>(p, kG1);
     const int mtiles = p.mtile_off[p.E];
     const int total = mtiles * NT;
@@ -721,7 +723,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
 // entries earlier in the list and every workgroup is resident (one per CU),
 // so the waits always end; a wait longer than kSpinLimit polls stops, sets
 // *p.status and lets the tile run (its output is then wrong, never a hang).
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool kIL>
 __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     const int tid = threadIdx.x;
@@ -736,7 +738,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams 
         int mt, ntile;
         cur.tile(tile, NT1, NT2, &mt, &ntile);
         if (cur.sg.g1) {
-            gemm_tile<BM, BN, WM, WN, true, true>(p, mt, ntile, smem);
+            gemm_tile<BM, BN, WM, WN, true, true, kIL>(p, mt, ntile, smem);
             // every thread's coherent h stores have completed (vmcnt(0)) before the barrier
             __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8) | (0 << 14));
             __syncthreads();
@@ -755,7 +757,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams 
                 }
             }
             __syncthreads();
-            gemm_tile<BM, BN, WM, WN, false, true>(p, mt, ntile, smem);
+            gemm_tile<BM, BN, WM, WN, false, true, false>(p, mt, ntile, smem);
         }
     }
 }
@@ -765,6 +767,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams 
 // 128-row m-tiles waste fewer padding rows on ragged expert segments than
 // 256-row ones, at the MFMA work per K step of a 256 x 256 tile.
 constexpr int kBM = 128, kBN = 512, kWM = 2, kWN = 4;
+static_assert(kBM == kTileRows, "the workspace tables are sized for kTileRows-row m-tiles");
 
 int gemm_bm() { return kBM; }
 
@@ -778,10 +781,10 @@ static hipError_t allow_lds(const void* kern, int bytes, DeviceCache& done) {
     }, &ok);
 }
 
-template <bool kG1>
+template <bool kG1, bool kIL>
 static hipError_t launch_gemm(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     using C = Cfg<kBM, kBN, kWM, kWN, kG1>;
-    auto kern = grouped_gemm_kernel<kBM, kBN, kWM, kWN, kG1>;
+    auto kern = grouped_gemm_kernel<kBM, kBN, kWM, kWN, kG1, kIL>;
     const size_t lds = (size_t)C::kLds;
     static DeviceCache lds_set;
     hipError_t err = allow_lds((const void*)kern, (int)lds, lds_set);
@@ -797,15 +800,16 @@ static hipError_t launch_gemm(const GemmParams& p, hipStream_t s, hipEvent_t ev0
 }
 
 hipError_t launch_gemm1(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    return launch_gemm<true>(p, s, ev0, ev1);
+    return p.w13_il ? launch_gemm<true, true>(p, s, ev0, ev1) : launch_gemm<true, false>(p, s, ev0, ev1);
 }
 hipError_t launch_gemm2(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    return launch_gemm<false>(p, s, ev0, ev1);
+    return launch_gemm<false, false>(p, s, ev0, ev1);
 }
 
-hipError_t launch_fused_gemm(const GemmParams& p_in, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+template <bool kIL>
+static hipError_t launch_fused(const GemmParams& p_in, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     using C = Cfg<kBM, kBN, kWM, kWN, true>;
-    auto kern = fused_gemm_kernel<kBM, kBN, kWM, kWN>;
+    auto kern = fused_gemm_kernel<kBM, kBN, kWM, kWN, kIL>;
     const size_t lds = (size_t)C::kLds;
     static DeviceCache lds_set;
     hipError_t err = allow_lds((const void*)kern, (int)lds, lds_set);
@@ -822,6 +826,10 @@ hipError_t launch_fused_gemm(const GemmParams& p_in, hipStream_t s, hipEvent_t e
     const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(upper, cus));
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(C::kThreads), lds, s, ev0, ev1, 0, p);
     return hipGetLastError();
+}
+
+hipError_t launch_fused_gemm(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    return p.w13_il ? launch_fused<true>(p, s, ev0, ev1) : launch_fused<false>(p, s, ev0, ev1);
 }
 
 }  // namespace moe

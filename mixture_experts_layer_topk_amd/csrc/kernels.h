@@ -102,7 +102,8 @@ struct GemmParams {
     int64_t w13sf_rs, w13sf_ks, w2sf_rs, w2sf_ks;
 };
 
-int gemm_bm();                  // rows per m-tile of the grouped GEMMs
+constexpr int kTileRows = 128;  // rows per m-tile of the tiled grouped GEMMs
+int gemm_bm();                  // the same, as the GEMM source defines it (== kTileRows)
 
 // Launch facts cached per device (CU counts, occupancies, "attribute set"):
 // the entry for the current device is filled by fill(dev, &value) on first use.
