@@ -48,6 +48,7 @@ extern "C" {
 #define MOE_EWORKSPACE (-3)    /* workspace too small or misaligned */
 #define MOE_EHIP (-4)          /* HIP runtime / launch failure */
 #define MOE_ETIMEOUT (-5)      /* moe_check_status: a bounded wait inside the last call gave up */
+#define MOE_ESCRATCH (-6)      /* moe_route_noalloc: T * topk above its static scratch's limit */
 
 #define MOE_SCORE_SOFTMAX 0
 #define MOE_SCORE_SIGMOID 1
@@ -237,6 +238,22 @@ int moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t s);
 int moe_route(const moe_dims_t* d, const float* logits, int32_t* topk_idx, float* topk_w,
               int32_t* counts, int32_t* offsets, int32_t* slot_src, int32_t* slot_of,
               void* ws, size_t ws_bytes, hipStream_t s);
+
+/* moe_route without a workspace, for callers that cannot allocate device memory
+ * or pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * moe_route, minus ws and ws_bytes.  The routing counters and tables live in a
+ * static device array of the library (about 2.4 MiB per device, held until the
+ * process ends), sized for T * topk <= 262144 routed pairs with any E <= 1024;
+ * a larger call returns MOE_ESCRATCH before anything is enqueued.  The call
+ * allocates nothing: it enqueues a small fill kernel that zeroes the array's
+ * counters, then the routing kernels.  Every call on one device shares that
+ * device's array, so two calls that may overlap on one device (different
+ * streams, or one stream while another call is in flight elsewhere) race and
+ * must be ordered by the caller. */
+int moe_route_noalloc(const moe_dims_t* d, const float* logits, int32_t* topk_idx, float* topk_w,
+                      int32_t* counts, int32_t* offsets, int32_t* slot_src, int32_t* slot_of,
+                      hipStream_t s);
 
 /* Per-row activation quantisation ("MegaMoE" notes, "Dispatch阶段"): each group
  * of 32 consecutive elements of a row gets the smallest power-of-two scale s

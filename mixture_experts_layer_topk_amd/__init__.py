@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
-MOE_ETIMEOUT = -5
+MOE_ETIMEOUT, MOE_ESCRATCH = -5, -6
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 FLAG_NONE, FLAG_NARROW, FLAG_TILED, FLAG_ONE_LAUNCH, FLAG_ONE_KERNEL = 0, 1, 2, 4, 8
 FLAG_W13_PREINTERLEAVED, FLAG_W_SCALES_PER_ROW = 16, 32
@@ -56,7 +56,7 @@ class Layout(ctypes.Structure):
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_workspace_size", "moe_workspace_layout", "moe_workspace_init", "moe_route",
-           "moe_quant_act", "moe_pack_weights", "moe_scales_kmajor", "moe_forward",
+           "moe_route_noalloc", "moe_quant_act", "moe_pack_weights", "moe_scales_kmajor", "moe_forward",
            "moe_check_status", "moe_error_string")
 
 
@@ -70,6 +70,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_workspace_layout.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Layout)]
     lib.moe_workspace_init.argtypes = [vp, sz, vp]
     lib.moe_route.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_route_noalloc.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_quant_act.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_pack_weights.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_scales_kmajor.argtypes = [vp, i64, i32, i32, vp, vp]
@@ -180,6 +181,22 @@ def route(d: Dims, logits: torch.Tensor, ws: torch.Tensor):
     _check(_lib.moe_route(ctypes.byref(d), _ptr(logits), _ptr(out["topk_idx"]), _ptr(out["topk_w"]),
                           _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["slot_src"]),
                           _ptr(out["slot_of"]), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def route_noalloc(d: Dims, logits: torch.Tensor):
+    """route() without a workspace (moe_route_noalloc: the library's static scratch)."""
+    T, k, E = d.T, d.topk, d.E
+    dev = logits.device
+    out = dict(topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+               topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+               counts=torch.empty(E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               slot_src=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
+               slot_of=torch.empty((T, k), dtype=torch.int32, device=dev))
+    _check(_lib.moe_route_noalloc(ctypes.byref(d), _ptr(logits), _ptr(out["topk_idx"]),
+                                  _ptr(out["topk_w"]), _ptr(out["counts"]), _ptr(out["offsets"]),
+                                  _ptr(out["slot_src"]), _ptr(out["slot_of"]), _stream()))
     return out
 
 

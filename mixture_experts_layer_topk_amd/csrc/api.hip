@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/moe.h: argument checks, the
 // workspace carve, and the launch sequence of the layer.
+#include <atomic>
 #include <string>
 
 #include "moe.h"
@@ -100,6 +101,123 @@ __global__ void zero_kernel(uint4* p, size_t n16) {
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off); }
 
+// Regions of the routing step inside a scratch buffer (byte offsets).
+struct RouteRegions {
+    size_t cnt, arrive, status, mtile_off, mtile_e, mtile_rec, sub_rec, nsub, ready, slot_in_e, slot_w;
+};
+
+// Routing and bucketisation of d's logits into the caller's outputs, with the
+// counters and tables in `base` at regions r.
+hipError_t launch_route_into(const moe_dims_t& d, const float* logits, int32_t* topk_idx, float* topk_w,
+                             int32_t* counts, int32_t* offsets, int32_t* slot_src, int32_t* slot_of,
+                             uint8_t* base, const RouteRegions& r, hipStream_t s) {
+    moe::RouteParams rp{};
+    rp.logits = logits;
+    rp.idx_out = topk_idx;
+    rp.w_out = topk_w;
+    rp.cnt = reinterpret_cast<int*>(base + r.cnt);
+    rp.slot_in_e = reinterpret_cast<int32_t*>(base + r.slot_in_e);
+    rp.T = d.T;
+    rp.H = d.H;
+    rp.E = d.E;
+    rp.topk = d.topk;
+    rp.score_fn = d.score_fn;
+    rp.renorm = d.renorm;
+    moe::ScatterParams sp{};
+    sp.idx = topk_idx;
+    sp.slot_in_e = rp.slot_in_e;
+    sp.cnt = rp.cnt;
+    sp.arrive = reinterpret_cast<unsigned*>(base + r.arrive);
+    sp.counts_out = counts;
+    sp.offsets_out = offsets;
+    sp.mtile_off = reinterpret_cast<int32_t*>(base + r.mtile_off);
+    sp.mtile_e = reinterpret_cast<int32_t*>(base + r.mtile_e);
+    sp.slot_src = slot_src;
+    sp.slot_of = slot_of;
+    sp.wts = topk_w;
+    sp.slot_w = reinterpret_cast<float*>(base + r.slot_w);
+    sp.T = d.T;
+    sp.E = d.E;
+    sp.topk = d.topk;
+    sp.bm = moe::gemm_bm();
+    sp.mtile_rec = reinterpret_cast<int4*>(base + r.mtile_rec);
+    sp.max_mtiles = (int)max_mtiles(d);
+    sp.sub_rec = reinterpret_cast<int4*>(base + r.sub_rec);
+    sp.nsub = reinterpret_cast<int32_t*>(base + r.nsub);
+    sp.max_subs = (int)max_subs(d);
+    sp.nready = (int)std::max(max_mtiles(d), max_subs(d));
+    sp.ready = reinterpret_cast<int*>(base + r.ready);
+    sp.status = reinterpret_cast<int*>(base + r.status);
+    return moe::launch_route(rp, sp, s);
+}
+
+// ---------------------------------------------------------------- routing without allocation
+// moe_route_noalloc keeps the routing step's counters and tables in a file-scope
+// device array instead of a caller's workspace, for callers that cannot
+// allocate.  Sized for T * topk <= kNoAllocMaxPairs with any E <= 1024.
+constexpr int64_t kNoAllocMaxPairs = int64_t(1) << 18;
+
+constexpr size_t align256(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct RouteCarve {
+    RouteRegions r;
+    size_t total;
+};
+
+// The routing regions alone, laid out as carve() lays them out: the counter
+// header (cnt, arrive, status) first.
+constexpr RouteCarve carve_route(int64_t R, int64_t E) {
+    const int64_t nonempty = E < R ? E : R;
+    const int64_t mtiles = (R + moe::kTileRows - 1) / moe::kTileRows + nonempty;
+    const int64_t subs = (R + moe::kSubRows - 1) / moe::kSubRows + nonempty;
+    RouteCarve c{};
+    size_t at = 0;
+    c.r.cnt = at;       at = align256(at + moe::kMaxExpertsCap * 4);
+    c.r.arrive = at;    at = align256(at + 64);
+    c.r.status = at;    at = align256(at + 64);
+    c.r.mtile_off = at; at = align256(at + (size_t)(E + 1) * 4);
+    c.r.mtile_e = at;   at = align256(at + (size_t)(mtiles + 1) * 4);
+    c.r.mtile_rec = at; at = align256(at + (size_t)(mtiles + 1) * 16);
+    c.r.sub_rec = at;   at = align256(at + (size_t)(subs + 1) * 16);
+    c.r.nsub = at;      at = align256(at + 4);
+    c.r.ready = at;     at = align256(at + (size_t)(mtiles > subs ? mtiles : subs) * 4);
+    c.r.slot_in_e = at; at = align256(at + (size_t)R * 4);
+    c.r.slot_w = at;    at = align256(at + (size_t)R * 4);
+    c.total = at;
+    return c;
+}
+
+constexpr size_t kScratchBytes = carve_route(kNoAllocMaxPairs, moe::kMaxExpertsCap).total;   // ~2.4 MiB
+
+}  // namespace
+
+// The no-allocation routing scratch: one copy per device, held until the process
+// ends, shared by every moe_route_noalloc call on that device.  Host code never
+// uses this name as an address: scratch_address() looks up each device's copy.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::atomic<void*> g_scratch[moe::kMaxDevices];
+
+// Device address of the current device's scratch, looked up once per device
+// (hipGetSymbolAddress with that device current) and kept.
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= moe::kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -152,44 +270,35 @@ int moe_route(const moe_dims_t* d, const float* logits, int32_t* topk_idx, float
         return MOE_EINVAL;
     Carve c = carve(*d);
     if (ws_bytes < c.total || ((uintptr_t)ws % kAlign) != 0) return MOE_EWORKSPACE;
-    moe::RouteParams rp{};
-    rp.logits = logits;
-    rp.idx_out = topk_idx;
-    rp.w_out = topk_w;
-    rp.cnt = at<int>(ws, c.cnt);
-    rp.slot_in_e = at<int32_t>(ws, c.slot_in_e);
-    rp.T = d->T;
-    rp.H = d->H;
-    rp.E = d->E;
-    rp.topk = d->topk;
-    rp.score_fn = d->score_fn;
-    rp.renorm = d->renorm;
-    moe::ScatterParams sp{};
-    sp.idx = topk_idx;
-    sp.slot_in_e = rp.slot_in_e;
-    sp.cnt = rp.cnt;
-    sp.arrive = at<unsigned>(ws, c.arrive);
-    sp.counts_out = counts;
-    sp.offsets_out = offsets;
-    sp.mtile_off = at<int32_t>(ws, c.mtile_off);
-    sp.mtile_e = at<int32_t>(ws, c.mtile_e);
-    sp.slot_src = slot_src;
-    sp.slot_of = slot_of;
-    sp.wts = topk_w;
-    sp.slot_w = at<float>(ws, c.slot_w);
-    sp.T = d->T;
-    sp.E = d->E;
-    sp.topk = d->topk;
-    sp.bm = moe::gemm_bm();
-    sp.mtile_rec = at<int4>(ws, c.mtile_rec);
-    sp.max_mtiles = (int)max_mtiles(*d);
-    sp.sub_rec = at<int4>(ws, c.sub_rec);
-    sp.nsub = at<int32_t>(ws, c.nsub);
-    sp.max_subs = (int)max_subs(*d);
-    sp.nready = (int)std::max(max_mtiles(*d), max_subs(*d));
-    sp.ready = at<int>(ws, c.ready);
-    sp.status = at<int>(ws, c.status);
-    hipError_t err = moe::launch_route(rp, sp, s);
+    RouteRegions r{c.cnt, c.arrive, c.status, c.mtile_off, c.mtile_e, c.mtile_rec, c.sub_rec, c.nsub,
+                   c.ready, c.slot_in_e, c.slot_w};
+    hipError_t err = launch_route_into(*d, logits, topk_idx, topk_w, counts, offsets, slot_src, slot_of,
+                                       static_cast<uint8_t*>(ws), r, s);
+    return err == hipSuccess ? MOE_OK : hip_fail(err);
+}
+
+int moe_route_noalloc(const moe_dims_t* d, const float* logits, int32_t* topk_idx, float* topk_w,
+                      int32_t* counts, int32_t* offsets, int32_t* slot_src, int32_t* slot_of,
+                      hipStream_t s) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if (!logits || !topk_idx || !topk_w || !counts || !offsets || !slot_src || !slot_of)
+        return MOE_EINVAL;
+    if (d->T * d->topk > kNoAllocMaxPairs) return MOE_ESCRATCH;
+    const RouteCarve c = carve_route(d->T * d->topk, d->E);
+    if (c.total > kScratchBytes) return MOE_ESCRATCH;
+    void* base = nullptr;
+    hipError_t err = scratch_address(&base);
+    if (err == hipSuccess) {
+        // the counter header must be zero on entry: every call clears it with a
+        // fill kernel (no memset node, so the call can be captured in a graph)
+        const size_t n16 = (c.r.status + 64) / 16;
+        hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(256), 0, s, static_cast<uint4*>(base), n16);
+        err = hipGetLastError();
+    }
+    if (err == hipSuccess)
+        err = launch_route_into(*d, logits, topk_idx, topk_w, counts, offsets, slot_src, slot_of,
+                                static_cast<uint8_t*>(base), c.r, s);
     return err == hipSuccess ? MOE_OK : hip_fail(err);
 }
 
@@ -391,6 +500,7 @@ const char* moe_error_string(int code) {
         case MOE_EUNSUPPORTED: return "unsupported shape";
         case MOE_EWORKSPACE: return "workspace too small or misaligned";
         case MOE_ETIMEOUT: return "a bounded wait inside the last call gave up (its output is invalid)";
+        case MOE_ESCRATCH: return "T * topk exceeds the 262144 routed pairs the static routing scratch holds";
         case MOE_EHIP: return g_hip_error.empty() ? "HIP error" : g_hip_error.c_str();
         default: return "unknown error";
     }

@@ -96,9 +96,19 @@ def test_quant_and_pack_reject_bad_sizes():
 
 def test_error_strings():
     m = _lib()
-    for code in (0, -1, -2, -3, -4, -5, -99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -99):
         assert m._lib.moe_error_string(code)
     assert b"wait" in m._lib.moe_error_string(m.MOE_ETIMEOUT)
+    assert b"scratch" in m._lib.moe_error_string(m.MOE_ESCRATCH)
+
+
+def test_route_noalloc_rejects_beyond_its_scratch_without_gpu():
+    m = _lib()
+    p = ctypes.c_void_p(1 << 20)                                               # never dereferenced
+    big = m.dims(32769, 128, 128, 64, 8)                                       # 262152 routed pairs
+    assert m._lib.moe_route_noalloc(ctypes.byref(big), p, p, p, p, p, p, p, None) == m.MOE_ESCRATCH
+    d = m.dims(16, 128, 128, 8, 2)
+    assert m._lib.moe_route_noalloc(ctypes.byref(d), None, p, p, p, p, p, p, None) == m.MOE_EINVAL
 
 
 def test_check_status_rejects_bad_workspace_without_gpu():
