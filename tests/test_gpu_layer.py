@@ -277,7 +277,9 @@ def test_forward_full256_every_expert_tail(flags):
     inter = dl.intermediates()
     counts = inter["counts"]
     ragged = int(((counts % 128) != 0).sum())
-    toks = _full256_tokens(inter, w)
+    if ("full256", "tokens") not in _BIG:
+        _BIG[("full256", "tokens")] = _full256_tokens(inter, w)
+    toks = _BIG[("full256", "tokens")]
     _log(f"  {len(toks)} tokens; {ragged} of {w.E} experts end in a partial m-tile; "
          f"{_fused_waves(w)} expert waves")
     dl2, ref = _big("full256", toks)
@@ -341,6 +343,7 @@ def test_weight_layout_flags(w):
     _log(f"weight layout flags {w.name}")
     dl = G.DeviceLayer(w)
     ref = _oracle_full(w)
+    G.prefetch_oracle_experts(w)
     q13 = np.stack([G.oracle_expert(w, e)[0] for e in range(w.E)])
     s13 = np.stack([G.oracle_expert(w, e)[1] for e in range(w.E)])
     iq, isf = M.interleave_w13(q13, s13)
