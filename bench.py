@@ -227,6 +227,26 @@ def _roofline(w, counts, gemm1_ms, stage_ms, path):
             "alg_bytes": alg_bytes}
 
 
+def hbm_ceiling(m, torch, hip, stream, nbytes: int, flush, steps: int):
+    """The HBM read ceiling of a footprint: moe_stream_read of nbytes from a buffer
+    no one has touched since the cache-evicting read, timed by the events its launch
+    carries, mean over ``steps`` (the same eviction as the timed steps before each)."""
+    nbytes = max(16, nbytes // 16 * 16)
+    probe = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    for i in range(steps):
+        if flush is not None:
+            flush.max()
+        m.stream_read(probe, sink, stream, evs[i][0], evs[i][1])
+    torch.cuda.synchronize()
+    us = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs])) * 1e3
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "stream_read_kernel (16-byte loads, nothing else)", "bytes": nbytes,
+            "kernel_us": round(us, 2), "achieved": round(gbs, 1), "unit": "GB/s",
+            "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(w, sample_experts: int):
     """The oracle, timed on a bounded sample of the workload and scaled to tokens/s.
 
@@ -388,6 +408,12 @@ def main():
                                for q, pq in (("p10", 10), ("p50", 50), ("p90", 90))},
         "roofline": roofline(w, counts, stage_ms, a.gemm_path, kernel_ms),
     }
+    out["us_per_step"] = round(ms * 1e3, 2)
+    if out["roofline"]["bound"] == "hbm":
+        # the same footprint read with nothing else to do: the ceiling beside the peak
+        ceil = hbm_ceiling(m, torch, hip, stream, int(out["roofline"]["alg_bytes"]), flush, a.steps)
+        out["roofline"]["ceiling"] = ceil
+        out["roofline"]["frac_of_ceiling"] = round(out["roofline"]["achieved"] / ceil["achieved"], 4)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_experts)
     print(json.dumps(out), flush=True)

@@ -308,6 +308,19 @@ int moe_forward(const moe_args_t* a, hipStream_t s);
  * misaligned ws, or MOE_EHIP. */
 int moe_check_status(const void* ws, hipStream_t s);
 
+/* Measurement helper: read `bytes` from src once with 16-byte loads spread over
+ * the GPU and nothing else to do (the HBM read ceiling of a footprint, the
+ * yardstick beside the roofline of a weight-streaming kernel).
+ *   src    device, 16-byte aligned; bytes a multiple of 16
+ *   sink   device uint32, left unchanged by real data (a store on one value
+ *          keeps the loads from being optimised away)
+ *   start, stop  NULL, or caller-created events the launch carries
+ *          (hipExtLaunchKernel): they take the kernel's start and end times
+ * MOE_EINVAL for bad pointers or sizes; bytes == 0 launches nothing (the
+ * events are then recorded on s). */
+int moe_stream_read(const void* src, size_t bytes, uint32_t* sink, hipEvent_t start, hipEvent_t stop,
+                    hipStream_t s);
+
 /* Static text for a return code (for MOE_EHIP: the calling thread's last HIP
  * error message). */
 const char* moe_error_string(int code);

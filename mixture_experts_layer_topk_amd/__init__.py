@@ -57,7 +57,7 @@ class Layout(ctypes.Structure):
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_workspace_size", "moe_workspace_layout", "moe_workspace_init", "moe_route",
            "moe_route_noalloc", "moe_quant_act", "moe_pack_weights", "moe_scales_kmajor", "moe_forward",
-           "moe_check_status", "moe_error_string")
+           "moe_check_status", "moe_stream_read", "moe_error_string")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -76,6 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_scales_kmajor.argtypes = [vp, i64, i32, i32, vp, vp]
     lib.moe_forward.argtypes = [ctypes.POINTER(Args), vp]
     lib.moe_check_status.argtypes = [vp, vp]
+    lib.moe_stream_read.argtypes = [vp, sz, vp, vp, vp, vp]
     lib.moe_error_string.argtypes = [ctypes.c_int]
     lib.moe_error_string.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -227,6 +228,13 @@ def forward(d: Dims, x, w13, w13_sf, w2, w2_sf, ws, logits=None, topk_idx=None, 
     forward_raw(forward_args(d, x, w13, w13_sf, w2, w2_sf, y, ws, logits, topk_idx, topk_w,
                              flags=flags))
     return y
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None, start=None, stop=None):
+    """Read src's bytes once (moe_stream_read: the HBM read ceiling of a footprint);
+    start/stop: None or hipEvent_t handles the launch carries."""
+    _check(_lib.moe_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), start, stop,
+                                stream if stream is not None else _stream()))
 
 
 def check_status(ws: torch.Tensor) -> int:

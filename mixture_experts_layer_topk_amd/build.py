@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "quant.hip", "gemm.hip", "narrow.hip", "combine.hip", "layer.hip"]
+SOURCES = ["api.hip", "route.hip", "quant.hip", "gemm.hip", "narrow.hip", "combine.hip", "layer.hip",
+           "stream.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -480,6 +480,14 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     return err == hipSuccess ? MOE_OK : hip_fail(err);
 }
 
+int moe_stream_read(const void* src, size_t bytes, uint32_t* sink, hipEvent_t start, hipEvent_t stop,
+                    hipStream_t s) {
+    if (bytes % 16 != 0) return MOE_EINVAL;
+    if (bytes && (!src || !sink || !aligned16(src) || ((uintptr_t)sink & 3))) return MOE_EINVAL;
+    hipError_t err = moe::launch_stream_read(src, bytes, sink, s, start, stop);
+    return err == hipSuccess ? MOE_OK : hip_fail(err);
+}
+
 int moe_check_status(const void* ws, hipStream_t s) {
     if (!ws || ((uintptr_t)ws % kAlign) != 0) return MOE_EINVAL;
     // the header's offsets do not depend on the shape: any valid shape gives them

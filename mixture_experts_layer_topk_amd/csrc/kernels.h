@@ -157,6 +157,11 @@ hipError_t launch_narrow_gemm2(const GemmParams& p, hipStream_t s, hipEvent_t ev
 hipError_t launch_narrow_fused(const GemmParams& p, hipStream_t s, hipEvent_t ev0 = nullptr,
                                hipEvent_t ev1 = nullptr);
 
+// Read `bytes` (a multiple of 16) from src once, with nothing else to do (the
+// HBM read ceiling of a footprint); sink takes a flag no real data sets.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s,
+                              hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+
 hipError_t launch_combine(const uint16_t* o, const int32_t* slot_of, int64_t T, int topk, int H,
                           uint16_t* y, hipStream_t s);
 
