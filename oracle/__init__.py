@@ -10,6 +10,8 @@ computes, following the pages' description step by step:
   codecs   E4M3 / E2M1 / E8M0 formats and the power-of-two block quantiser
   moe_ref  routing, counting-sort bucketisation, activation quantisation,
            grouped GEMM1 + SwiGLU*weight epilogue, grouped GEMM2, combine
+  blockfp8 the block-FP8 (128 x 128 weight blocks, float32 scales) variant of
+           the expert MLP, on moe_ref's routing, bucketisation and combine
 
 Sources (web pages, cited by title and section):
   [MegaMoE notes]  "MegaMoE" study notes (obnotes), sections "Dispatch阶段",
@@ -21,7 +23,8 @@ Sources (web pages, cited by title and section):
                    combine excerpts.
   [Counting sort]  "05.10 Counting Sort / Bucketization 在 DeepGEMM Mega MoE 中的映射",
                    sections 2.1-2.3, 5.2, 7.1, 9.1.
-  [MonoMoe]        "MonoMoe kernel — design", §1 (five-phase pipeline).
+  [MonoMoe]        "MonoMoe kernel — design", the fixed-shape paragraph (block-FP8
+                   128 x 128 weights) and §1 (five-phase pipeline).
 
 Parity status: every function here is pinned by tests under tests/ against
 format definitions, torch casts, brute force and invariants, except the

@@ -178,3 +178,108 @@ def layer(x_bits, w13_bits, w2_bits, topk, I, logits=None, topk_idx=None,
         y.append(row)
     return dict(idx=idx, w=wts, counts=counts, xq=xq, xsf=xsf, hq=hq, hsf=hsf,
                 o=o, y=y, wq13=wq13, ws13=ws13, wq2=wq2, ws2=ws2)
+
+
+# ---------------------------------------------------------------- block-FP8 weights
+
+def f32_of_fraction(x: Fraction) -> float:
+    """x rounded to float32, nearest even, by exact search between float32 neighbours."""
+    if x == 0:
+        return 0.0
+    a = float(np.float32(float(x)))            # within one float32 step of the answer
+    cands = {a, float(np.nextafter(np.float32(a), np.float32(np.inf))),
+             float(np.nextafter(np.float32(a), np.float32(-np.inf)))}
+    best = min(cands, key=lambda c: (abs(Fraction(c) - x),
+                                     int(np.array([c], np.float32).view(np.uint32)[0]) & 1))
+    return best
+
+
+def quant_fp8_block(vals):
+    """vals: the exact values of one block -> (E4M3 codes, float32 scale): the scale is
+    max|v| / 448 rounded to float32 (1 for an all-zero block), each code the E4M3 value
+    nearest to v / s rounded to float32 (torch's cast), clamped to +-448."""
+    amax = max(abs(Fraction(v)) for v in vals)
+    s = f32_of_fraction(amax / 448) if amax else 1.0
+    codes = []
+    for v in vals:
+        q = f32_of_fraction(Fraction(v) / Fraction(s))
+        codes.append(e4m3_round(max(-448.0, min(448.0, q))))
+    return codes, s
+
+
+def layer_fp8b(x_bits, w13_bits, w2_bits, topk, I, logits):
+    """Loop model of the block-FP8 variant (128 x 128 weight blocks, 1 x 128 activation
+    groups, float32 scales), softmax routing renormalised.  Returns y and hq by (t, j)."""
+    T, H = len(x_bits), len(x_bits[0])
+    E = len(w13_bits)
+    B = 128
+
+    def qrow(row):
+        codes, scales = [], []
+        for g in range(0, len(row), B):
+            c, s = quant_fp8_block(row[g:g + B])
+            codes += c
+            scales.append(s)
+        return codes, scales
+
+    def qmat(m):
+        n, k = len(m), len(m[0])
+        codes = [[0] * k for _ in range(n)]
+        scales = [[0.0] * (k // B) for _ in range(n // B)]
+        for bi in range(n // B):
+            for bj in range(k // B):
+                vals = [m[bi * B + r][bj * B + c] for r in range(B) for c in range(B)]
+                cs, s = quant_fp8_block(vals)
+                scales[bi][bj] = s
+                for r in range(B):
+                    for c in range(B):
+                        codes[bi * B + r][bj * B + c] = cs[r * B + c]
+        return codes, scales
+
+    idx, wts = [], []
+    for t in range(T):
+        row = [float(v) for v in logits[t]]
+        order = sorted(range(E), key=lambda e: (-row[e], e))[:topk]
+        m = max(row)
+        z = [math.exp(v - m) for v in row]
+        tot = math.fsum(z)
+        s = [z[e] / tot for e in order]
+        tot = math.fsum(s)
+        idx.append(order)
+        wts.append([f32(v / tot) for v in s])
+    W13, W2 = [], []
+    for e in range(E):
+        W13.append(qmat([[bf16_to_float(int(b)) for b in r] for r in w13_bits[e]]))
+        W2.append(qmat([[bf16_to_float(int(b)) for b in r] for r in w2_bits[e]]))
+    hq, y = {}, []
+    o = {}
+    for t in range(T):
+        xc, xs = qrow([bf16_to_float(int(b)) for b in x_bits[t]])
+        # dequantised values and their products as exact rationals (a float32 scale
+        # times a code has up to 28 significant bits, a product up to 56)
+        a = [Fraction(e4m3_to_float(xc[h])) * Fraction(xs[h // B]) for h in range(H)]
+        for j in range(topk):
+            e = idx[t][j]
+            (c13, s13), (c2, s2) = W13[e], W2[e]
+            acc1 = [f32_of_fraction(sum(a[h] * Fraction(e4m3_to_float(c13[n][h])) * Fraction(s13[n // B][h // B])
+                                        for h in range(H)))
+                    for n in range(2 * I)]
+            h_row = []
+            for i in range(I):
+                g, u = acc1[i], acc1[I + i]
+                silu = g / (1.0 + math.exp(-g)) if g > -700 else 0.0 * g
+                h_row.append(f32(silu * u * wts[t][j]))
+            hc, hs = qrow(h_row)
+            hq[(t, j)] = (hc, hs)
+            a2 = [Fraction(e4m3_to_float(hc[i])) * Fraction(hs[i // B]) for i in range(I)]
+            o[(t, j)] = [bf16_round(f32_of_fraction(sum(a2[i] * Fraction(e4m3_to_float(c2[n][i])) *
+                                                        Fraction(s2[n // B][i // B]) for i in range(I))))
+                         for n in range(H)]
+        row = []
+        for n in range(H):
+            acc = np.float32(0.0)
+            for j in range(topk):
+                acc = np.float32(acc + np.float32(bf16_to_float(o[(t, j)][n])))
+            row.append(bf16_round(float(acc)))
+        y.append(row)
+    return dict(idx=idx, w=wts, hq=hq, y=y)

@@ -132,3 +132,48 @@ def test_combine_order_and_precision_mistakes_are_caught(monkeypatch, patch):
     monkeypatch.setattr(M, "combine", patch)
     with pytest.raises(AssertionError):
         TL.test_combine_adds_in_slot_order_in_fp32()
+
+
+# ---------------------------------------------------------------- block-FP8 oracle
+
+from oracle import blockfp8 as B  # noqa: E402
+from tests import test_oracle_blockfp8 as TB  # noqa: E402
+
+_ORIG_B_SCALE = B._scale
+_ORIG_B_DQW = B.dequant_weights
+
+
+def _scale_480(amax):
+    s = (np.asarray(amax, np.float64) / 480.0).astype(np.float32)
+    return np.where(np.asarray(amax) == 0, np.float32(1.0), s).astype(np.float32)
+
+
+def _dq_weights_transposed_scales(codes, s):
+    s = np.asarray(s)
+    if s.shape[-1] == s.shape[-2]:
+        s = np.swapaxes(s, -1, -2)
+    return _ORIG_B_DQW(codes, s)
+
+
+def test_block_scale_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(B, "_scale", _scale_480)
+    with pytest.raises(AssertionError):
+        TB.test_block_scale_is_amax_over_448_in_float32()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("patch", ["transposed_block_scales", "dropped_topk_weight"])
+def test_block_fp8_layer_mistakes_are_caught(monkeypatch, patch):
+    if patch == "transposed_block_scales":
+        # W2 of the tiny shape is one 128 x 128 block per expert, so transpose W13's
+        # [2, 1] scale grid instead: swap which half of the gate/up rows each scale covers
+        def dq(codes, s):
+            s = np.asarray(s)
+            if s.shape[-2] == 2:
+                s = s[..., ::-1, :]
+            return _ORIG_B_DQW(codes, s)
+        monkeypatch.setattr(B, "dequant_weights", dq)
+    else:
+        monkeypatch.setattr(M, "silu_mul_weight", _dropped_weight)
+    with pytest.raises(AssertionError):
+        TB._compare_with_brute()
