@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-sample-experts", type=int, default=24,
                     help="experts whose rows the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weights", choices=("fp4", "fp8-block128"), default="fp4",
+                    help="weight format: FP4 E2M1 + UE8M0/32 (the layer's), or the block-FP8 "
+                         "variant (E4M3, one float32 scale per 128 x 128 block; narrow GEMMs)")
     ap.add_argument("--gemm-path", choices=("auto", "narrow", "narrow-one-launch", "tiled", "one-launch",
                                             "one-kernel"),
                     default="auto", help="GEMM kernels moe_forward uses (default: its own choice)")
@@ -97,17 +100,25 @@ class Hip:
         return ms.value
 
 
-def setup_device(w, m, torch):
+def setup_device(w, m, torch, fmt="fp4"):
     import moe_workloads as W
     from concurrent.futures import ThreadPoolExecutor
 
     dev = "cuda"
     x = torch.from_numpy(W.gen_x(w).view(np.int16)).view(torch.bfloat16).to(dev)
     logits = torch.from_numpy(W.gen_logits(w)).to(dev)
-    w13q = torch.empty((w.E, 2 * w.I, w.H // 2), dtype=torch.uint8, device=dev)
-    w13sf = torch.empty((w.E, 2 * w.I, w.H // 32), dtype=torch.uint8, device=dev)
-    w2q = torch.empty((w.E, w.H, w.I // 2), dtype=torch.uint8, device=dev)
-    w2sf = torch.empty((w.E, w.H, w.I // 32), dtype=torch.uint8, device=dev)
+    fp8 = fmt == "fp8-block128"
+    if fp8:
+        w13q = torch.empty((w.E, 2 * w.I, w.H), dtype=torch.uint8, device=dev)
+        w13sf = torch.empty((w.E, 2 * w.I // 128, w.H // 128), dtype=torch.float32, device=dev)
+        w2q = torch.empty((w.E, w.H, w.I), dtype=torch.uint8, device=dev)
+        w2sf = torch.empty((w.E, w.H // 128, w.I // 128), dtype=torch.float32, device=dev)
+    else:
+        w13q = torch.empty((w.E, 2 * w.I, w.H // 2), dtype=torch.uint8, device=dev)
+        w13sf = torch.empty((w.E, 2 * w.I, w.H // 32), dtype=torch.uint8, device=dev)
+        w2q = torch.empty((w.E, w.H, w.I // 2), dtype=torch.uint8, device=dev)
+        w2sf = torch.empty((w.E, w.H, w.I // 32), dtype=torch.uint8, device=dev)
+    pack = m.pack_weights_fp8_block128 if fp8 else m.pack_weights
 
     def gen(e):
         return W.gen_expert_w13(w, e), W.gen_expert_w2(w, e)
@@ -117,9 +128,10 @@ def setup_device(w, m, torch):
 
     with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
         for e, (b13, b2) in enumerate(ex.map(gen, range(w.E))):
-            w13q[e], w13sf[e] = m.pack_weights(up(b13))
-            w2q[e], w2sf[e] = m.pack_weights(up(b2))
-    w13sf, w2sf = m.scales_kmajor(w13sf, w.H), m.scales_kmajor(w2sf, w.I)
+            w13q[e], w13sf[e] = pack(up(b13))
+            w2q[e], w2sf[e] = pack(up(b2))
+    if not fp8:
+        w13sf, w2sf = m.scales_kmajor(w13sf, w.H), m.scales_kmajor(w2sf, w.I)
     torch.cuda.synchronize()
     return x, logits, w13q, w13sf, w2q, w2sf
 
@@ -151,16 +163,22 @@ def read_traffic(workload: str):
     return float(kv["traffic_bytes_per_launch"])
 
 
-def gemm1_algorithmic_bytes(w, counts) -> float:
+def gemm1_algorithmic_bytes(w, counts, fmt="fp4") -> float:
     """Bytes GEMM1 must move at least: W1|W3 codes and scales of every expert that
-    receives a row, the quantised activations once, and the quantised h it writes."""
+    receives a row, the quantised activations once, and the h it writes (quantised;
+    float32 for block-FP8 weights, quantised per 128 by the next launch)."""
     touched = int((counts > 0).sum())
-    w13 = 2 * w.I * (w.H // 2 + w.H // 32)
     R = w.T * w.topk
+    if fmt == "fp8-block128":
+        w13 = 2 * w.I * w.H + (2 * w.I // 128) * (w.H // 128) * 4
+        return touched * w13 + w.T * (w.H + w.H // 32) + R * w.I * 4
+    w13 = 2 * w.I * (w.H // 2 + w.H // 32)
     return touched * w13 + w.T * (w.H + w.H // 32) + R * (w.I + w.I // 32)
 
 
-def gemm1_kernel_name(w, path) -> str:
+def gemm1_kernel_name(w, path, fmt="fp4") -> str:
+    if fmt == "fp8-block128":
+        return "narrow_w8_gemm_kernel<GEMM1> (weight-streaming block-FP8 MFMA + SwiGLU*w -> float32 h)"
     if path == "narrow" or (path == "auto" and w.T * w.topk <= NARROW_ROWS_PER_EXPERT * w.E):
         return "narrow_gemm_kernel<GEMM1> (weight-streaming FP8xFP4 MFMA + SwiGLU*w -> FP8)"
     return "grouped_gemm_kernel<GEMM1> (tiled FP8xFP4 MFMA + SwiGLU*w -> FP8)"
@@ -175,18 +193,18 @@ def layer_algorithmic_bytes(w, counts) -> float:
     return touched * (w13 + w2) + w.T * (2 * w.H + 4 * w.E + 2 * w.H)
 
 
-def roofline(w, counts, stage_ms, path="auto", kernel_ms=None):
+def roofline(w, counts, stage_ms, path="auto", kernel_ms=None, fmt="fp4"):
     """The dominant kernel's roofline.  Its time is kernel_ms, the mean duration
     of the GEMM1 launch from the start and end events that launch carries
     (no launch gaps, no stage events inside it); without it, the GEMM1 stage
     time."""
     gemm1_ms = float(kernel_ms) if kernel_ms is not None else float(stage_ms[1])
-    r = _roofline(w, counts, gemm1_ms, stage_ms, path)
+    r = _roofline(w, counts, gemm1_ms, stage_ms, path, fmt)
     r["kernel_us"] = round(gemm1_ms * 1e3, 2)
     return r
 
 
-def _roofline(w, counts, gemm1_ms, stage_ms, path):
+def _roofline(w, counts, gemm1_ms, stage_ms, path, fmt="fp4"):
     if path == "one-kernel":
         # the whole layer in one kernel: its minimum bytes over its duration
         ms = float(sum(stage_ms))
@@ -212,10 +230,10 @@ def _roofline(w, counts, gemm1_ms, stage_ms, path):
                 "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_FP8_TFLOPS, 4),
                 "traffic": None, "alg_bytes": None}
-    kernel = gemm1_kernel_name(w, path)
-    traffic = read_traffic(w.name)
-    alg_bytes = gemm1_algorithmic_bytes(w, counts)
-    if w.name in HBM_BOUND:
+    kernel = gemm1_kernel_name(w, path, fmt)
+    traffic = read_traffic(w.name) if fmt == "fp4" else None
+    alg_bytes = gemm1_algorithmic_bytes(w, counts, fmt)
+    if w.name in HBM_BOUND or fmt == "fp8-block128":
         gbs = alg_bytes / (gemm1_ms * 1e-3) / 1e9
         return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -247,7 +265,7 @@ def hbm_ceiling(m, torch, hip, stream, nbytes: int, flush, steps: int):
             "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
-def cpu_baseline(w, sample_experts: int):
+def cpu_baseline(w, sample_experts: int, fmt: str = "fp4"):
     """The oracle, timed on a bounded sample of the workload and scaled to tokens/s.
 
     Timed in full: routing, bucketisation and activation quantisation of all T
@@ -257,14 +275,20 @@ def cpu_baseline(w, sample_experts: int):
     the sampled experts' weights are generated and quantised (input preparation,
     not timed)."""
     import moe_workloads as W
+    from oracle import blockfp8 as B
     from oracle import moe_ref as M
+
+    fp8 = fmt == "fp8-block128"
+    quant_act = B.quant_act if fp8 else M.quant_act
+    pack = B.quant_weights if fp8 else M.pack_weights
+    expert_rows = B.expert_rows if fp8 else M.expert_rows
 
     x = W.gen_x(w)
     logits = W.gen_logits(w)
     t0 = time.perf_counter()
     idx, wts = M.route(logits, w.topk, w.score_fn, bool(w.renorm))
     counts, offsets, slot_src, slot_of = M.bucketize(idx, w.E)
-    xq, xsf = M.quant_act(x)
+    xq, xsf = quant_act(x)
     t_front = time.perf_counter() - t0
 
     experts = [e for e in range(w.E) if counts[e] > 0][:sample_experts]
@@ -272,13 +296,13 @@ def cpu_baseline(w, sample_experts: int):
     t_rows = 0.0
     o = np.zeros((int(offsets[w.E]), w.H), np.uint16)
     for e in experts:
-        q13, s13 = M.pack_weights(W.gen_expert_w13(w, e))
-        q2, s2 = M.pack_weights(W.gen_expert_w2(w, e))
+        q13, s13 = pack(W.gen_expert_w13(w, e))
+        q2, s2 = pack(W.gen_expert_w2(w, e))
         pos = np.arange(offsets[e], offsets[e + 1])
         f = slot_src[pos]
         t, j = f // w.topk, f % w.topk
         t0 = time.perf_counter()
-        _, _, _, o[pos] = M.expert_rows(xq[t], xsf[t], wts[t, j], q13, s13, q2, s2, w.I)
+        _, _, _, o[pos] = expert_rows(xq[t], xsf[t], wts[t, j], q13, s13, q2, s2, w.I)
         t_rows += time.perf_counter() - t0
         rows += len(pos)
     t0 = time.perf_counter()
@@ -313,7 +337,7 @@ def main():
         w = replace(w.with_tokens(a.tokens), name=f"{w.name}_T{a.tokens}")
     if a.flush_mb is None:
         a.flush_mb = 1024 if w.name in HBM_BOUND else 0
-    x, logits, w13q, w13sf, w2q, w2sf = setup_device(w, m, torch)
+    x, logits, w13q, w13sf, w2q, w2sf = setup_device(w, m, torch, a.weights)
     d = m.dims(w.T, w.H, w.I, w.E, w.topk, w.score_fn, w.renorm)
     ws = m.new_workspace(d)
     y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
@@ -329,6 +353,8 @@ def main():
     flags = {"auto": m.FLAG_NONE, "narrow": m.FLAG_NARROW, "tiled": m.FLAG_TILED,
              "one-launch": m.FLAG_ONE_LAUNCH, "one-kernel": m.FLAG_ONE_KERNEL,
              "narrow-one-launch": m.FLAG_NARROW | m.FLAG_ONE_LAUNCH}[a.gemm_path]
+    if a.weights == "fp8-block128":
+        flags |= m.FLAG_WEIGHTS_FP8_BLOCK128
     args_plain = m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, flags=flags)
     args_ev = [m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, flags=flags,
                               stage_events=e, kernel_events=kev[i] if kev else None)
@@ -396,17 +422,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3 x fp4e2m1 (ue8m0/32 scales), f32 accumulate",
+        "dtype": ("fp8e4m3 x fp4e2m1 (ue8m0/32 scales), f32 accumulate" if a.weights == "fp4" else
+                  "fp8e4m3 x fp8e4m3 (f32 scales per 128x128 weight block and per 1x128 activations), "
+                  "f32 accumulate"),
         "data": "synthetic (seeded N(0,1) x and logits, N(0,0.02) BF16 weights quantised on the GPU)",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "topk": w.topk,
                    "score_fn": "sigmoid" if w.score_fn else "softmax", "renorm": bool(w.renorm),
-                   "zipf_s": w.zipf_s, "parallelism": "single GPU"},
+                   "zipf_s": w.zipf_s, "weights": a.weights, "parallelism": "single GPU"},
         "layer_tflops": round(layer_tflops, 2),
         "layer_frac_mfma": round(layer_tflops / PEAK_MFMA_FP8_TFLOPS, 4),
         "stages_ms": {n: round(float(v), 4) for n, v in zip(m.STAGES, stage_ms)},
         "stage_pass_step_ms": {q: round(float(np.percentile(step_ms, pq)), 4)
                                for q, pq in (("p10", 10), ("p50", 50), ("p90", 90))},
-        "roofline": roofline(w, counts, stage_ms, a.gemm_path, kernel_ms),
+        "roofline": roofline(w, counts, stage_ms, a.gemm_path, kernel_ms, a.weights),
     }
     out["us_per_step"] = round(ms * 1e3, 2)
     if out["roofline"]["bound"] == "hbm":
@@ -415,7 +443,7 @@ def main():
         out["roofline"]["ceiling"] = ceil
         out["roofline"]["frac_of_ceiling"] = round(out["roofline"]["achieved"] / ceil["achieved"], 4)
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_experts)
+        out["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_experts, a.weights)
     print(json.dumps(out), flush=True)
 
 

@@ -131,6 +131,17 @@ typedef struct moe_dims {
 #define MOE_FLAG_W_SCALES_PER_ROW 32u
 #define MOE_FLAG_KEEP_INTERMEDIATES 64u
 #define MOE_FLAG_DEBUG_SPIN_BOUND 128u
+/* Block-FP8 weights ("MonoMoe kernel — design", the fixed-shape paragraph:
+ * block-FP8 128 x 128 weights, for the decode shape of at most 8 tokens): w13
+ * and w2 hold E4M3 codes [E, 2I, H] and [E, H, I], w13_sf and w2_sf one float32
+ * scale per 128 x 128 block, [E, 2I/128, H/128] and [E, H/128, I/128]
+ * (moe_pack_weights_fp8_block128 writes both).  x and h are quantised to E4M3
+ * with one float32 scale per row per 128 elements (scale = max|v| / 448).  The
+ * GEMMs run as the narrow kernels in two launches, with a quantisation launch
+ * for h between them (a 128-column group spans several workgroups' units).
+ * MOE_EUNSUPPORTED with TILED, ONE_LAUNCH or ONE_KERNEL; MOE_EINVAL with
+ * W13_PREINTERLEAVED or W_SCALES_PER_ROW. */
+#define MOE_FLAG_WEIGHTS_FP8_BLOCK128 256u
 
 #define MOE_NUM_STAGE_EVENTS 5
 
@@ -191,8 +202,10 @@ typedef struct moe_args {
  *   offsets   int32 [E + 1]       exclusive prefix sum of counts
  *   slot_src  int32 [T*topk]      t*topk + j of position p (first offsets[E] valid)
  *   slot_of   int32 [T, topk]     position of pair (t, j), -1 when skipped
- *   xq, xsf   uint8 [T, H], [H/128, T, 4]        quantised x (scales K-step major)
- *   hq, hsf   uint8 [T*topk, I], [I/128, T*topk, 4]  quantised h by position
+ *   xq, xsf   uint8 [T, H], [H/128, T, 4]        quantised x (scales K-step major;
+ *                                               float32 [H/128, T] with block-FP8 weights)
+ *   hq, hsf   uint8 [T*topk, I], [I/128, T*topk, 4]  quantised h by position (float32
+ *                                               [I/128, T*topk] with block-FP8 weights)
  *   o         BF16 [T*topk, H]                  GEMM2 rows by position
  *   status    int32 [1]   nonzero if a wait of the one-launch GEMMs gave up in
  *                         the last call (its output is then invalid); every
@@ -272,6 +285,18 @@ int moe_quant_act(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* q, uin
  *   sf  device uint8 [rows, cols/32] out */
 int moe_pack_weights(const uint16_t* w, int64_t rows, int32_t cols, uint8_t* q, uint8_t* sf,
                      hipStream_t s);
+
+/* Block-FP8 weight quantisation ("MonoMoe kernel — design", fixed-shape
+ * paragraph): BF16 [rows, cols] to E4M3 codes with one float32 scale per
+ * 128 x 128 block: s = max|v| / 448 over the block (1 for an all-zero block),
+ * codes nearest-even E4M3 of v / s.  A stack of matrices [E, N, K] is one
+ * [E * N, K] call when N is a multiple of 128.
+ *   w    device BF16 [rows, cols]; rows and cols multiples of 128
+ *   q    device uint8 [rows, cols] out
+ *   sf   device float32 [rows/128, cols/128] out
+ * MOE_EINVAL for bad sizes or pointers (w 16-byte, q 16-byte, sf 4-byte aligned). */
+int moe_pack_weights_fp8_block128(const uint16_t* w, int64_t rows, int32_t cols, uint8_t* q, float* sf,
+                                  hipStream_t s);
 
 /* Weight-scale layout change for moe_forward (the layer's counterpart of a
  * one-time weight transform): per-row scales [mats, rows, cols/32] become K-step

@@ -22,6 +22,7 @@ SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 FLAG_NONE, FLAG_NARROW, FLAG_TILED, FLAG_ONE_LAUNCH, FLAG_ONE_KERNEL = 0, 1, 2, 4, 8
 FLAG_W13_PREINTERLEAVED, FLAG_W_SCALES_PER_ROW = 16, 32
 FLAG_KEEP_INTERMEDIATES, FLAG_DEBUG_SPIN_BOUND = 64, 128
+FLAG_WEIGHTS_FP8_BLOCK128 = 256
 
 
 class MoeError(RuntimeError):
@@ -56,7 +57,8 @@ class Layout(ctypes.Structure):
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_workspace_size", "moe_workspace_layout", "moe_workspace_init", "moe_route",
-           "moe_route_noalloc", "moe_quant_act", "moe_pack_weights", "moe_scales_kmajor", "moe_forward",
+           "moe_route_noalloc", "moe_quant_act", "moe_pack_weights", "moe_pack_weights_fp8_block128",
+           "moe_scales_kmajor", "moe_forward",
            "moe_check_status", "moe_stream_read", "moe_error_string")
 
 
@@ -73,6 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_route_noalloc.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_quant_act.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_pack_weights.argtypes = [vp, i64, i32, vp, vp, vp]
+    lib.moe_pack_weights_fp8_block128.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_scales_kmajor.argtypes = [vp, i64, i32, i32, vp, vp]
     lib.moe_forward.argtypes = [ctypes.POINTER(Args), vp]
     lib.moe_check_status.argtypes = [vp, vp]
@@ -149,6 +152,17 @@ def pack_weights(w: torch.Tensor):
     q = torch.empty(w.shape[:-1] + (cols // 2,), dtype=torch.uint8, device=w.device)
     sf = torch.empty(w.shape[:-1] + (cols // 32,), dtype=torch.uint8, device=w.device)
     _check(_lib.moe_pack_weights(_ptr(w), rows, cols, _ptr(q), _ptr(sf), _stream()))
+    return q, sf
+
+
+def pack_weights_fp8_block128(w: torch.Tensor):
+    """w BF16 [..., N, K] (N, K multiples of 128) -> (E4M3 codes uint8 [..., N, K], float32
+    scales [..., N/128, K/128]): one scale per 128 x 128 block."""
+    cols = w.shape[-1]
+    rows = w.numel() // cols
+    q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    sf = torch.empty(w.shape[:-2] + (w.shape[-2] // 128, cols // 128), dtype=torch.float32, device=w.device)
+    _check(_lib.moe_pack_weights_fp8_block128(_ptr(w), rows, cols, _ptr(q), _ptr(sf), _stream()))
     return q, sf
 
 
@@ -246,8 +260,10 @@ def check_status(ws: torch.Tensor) -> int:
     return rc
 
 
-def intermediates(d: Dims, ws: torch.Tensor):
-    """Views of the workspace intermediates left by the last forward with ws."""
+def intermediates(d: Dims, ws: torch.Tensor, block_fp8: bool = False):
+    """Views of the workspace intermediates left by the last forward with ws
+    (block_fp8: the forward ran with FLAG_WEIGHTS_FP8_BLOCK128, whose xsf and hsf are
+    float32, one per row per 128 elements)."""
     L = workspace_layout(d)
     T, k, E, H, I = d.T, d.topk, d.E, d.H, d.I
     R = T * k
@@ -256,6 +272,13 @@ def intermediates(d: Dims, ws: torch.Tensor):
         nbytes = n * torch.tensor([], dtype=dtype).element_size()
         return ws[off:off + nbytes].view(dtype).view(shape)
 
+    if block_fp8:
+        xsf = view(L.xsf, T * H // 128, torch.float32, (H // 128, T)).t()
+        hsf = view(L.hsf, R * I // 128, torch.float32, (I // 128, R)).t()
+    else:
+        # scales are K-step major in the workspace; shown here per row
+        xsf = view(L.xsf, T * H // 32, torch.uint8, (H // 128, T, 4)).permute(1, 0, 2).reshape(T, H // 32)
+        hsf = view(L.hsf, R * I // 32, torch.uint8, (I // 128, R, 4)).permute(1, 0, 2).reshape(R, I // 32)
     return dict(
         topk_idx=view(L.topk_idx, R, torch.int32, (T, k)),
         topk_w=view(L.topk_w, R, torch.float32, (T, k)),
@@ -264,10 +287,9 @@ def intermediates(d: Dims, ws: torch.Tensor):
         slot_src=view(L.slot_src, R, torch.int32, (R,)),
         slot_of=view(L.slot_of, R, torch.int32, (T, k)),
         xq=view(L.xq, T * H, torch.uint8, (T, H)),
-        # scales are K-step major in the workspace; shown here per row
-        xsf=view(L.xsf, T * H // 32, torch.uint8, (H // 128, T, 4)).permute(1, 0, 2).reshape(T, H // 32),
+        xsf=xsf,
         hq=view(L.hq, R * I, torch.uint8, (R, I)),
-        hsf=view(L.hsf, R * I // 32, torch.uint8, (I // 128, R, 4)).permute(1, 0, 2).reshape(R, I // 32),
+        hsf=hsf,
         o=view(L.o, R * H, torch.int16, (R, H)),
         status=view(L.status, 1, torch.int32, (1,)),
     )

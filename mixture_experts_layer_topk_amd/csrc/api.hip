@@ -70,7 +70,9 @@ Carve carve(const moe_dims_t& d) {
     c.xsf = take(T * (size_t)d.H / 32);
     c.hq = take(R * (size_t)d.I);
     c.hsf = take(R * (size_t)d.I / 32);
-    c.o = take(R * (size_t)d.H * 2);
+    // o is BF16 [R, H]; with block-FP8 weights the same bytes first hold GEMM1's
+    // float32 h [R, I] (quantised before GEMM2 writes o)
+    c.o = take(R * std::max((size_t)d.H * 2, (size_t)d.I * 4));
     c.total = at;
     return c;
 }
@@ -320,6 +322,15 @@ int moe_pack_weights(const uint16_t* w, int64_t rows, int32_t cols, uint8_t* q, 
     return err == hipSuccess ? MOE_OK : hip_fail(err);
 }
 
+int moe_pack_weights_fp8_block128(const uint16_t* w, int64_t rows, int32_t cols, uint8_t* q, float* sf,
+                                  hipStream_t s) {
+    if (rows < 0 || cols <= 0 || rows % 128 != 0 || cols % 128 != 0) return MOE_EINVAL;
+    if (rows == 0) return MOE_OK;
+    if (!w || !q || !sf || !aligned16(w) || !aligned16(q) || ((uintptr_t)sf & 3)) return MOE_EINVAL;
+    hipError_t err = moe::launch_pack_block128(w, rows, cols, q, sf, s);
+    return err == hipSuccess ? MOE_OK : hip_fail(err);
+}
+
 int moe_scales_kmajor(const uint8_t* sf, int64_t mats, int32_t rows, int32_t cols, uint8_t* out,
                       hipStream_t s) {
     if (mats < 0 || rows < 0 || cols <= 0 || cols % 128 != 0) return MOE_EINVAL;
@@ -340,11 +351,15 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     const uint32_t f = a->flags;
     const uint32_t known = MOE_FLAG_NARROW | MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH | MOE_FLAG_ONE_KERNEL |
                            MOE_FLAG_W13_PREINTERLEAVED | MOE_FLAG_W_SCALES_PER_ROW |
-                           MOE_FLAG_KEEP_INTERMEDIATES | MOE_FLAG_DEBUG_SPIN_BOUND;
+                           MOE_FLAG_KEEP_INTERMEDIATES | MOE_FLAG_DEBUG_SPIN_BOUND |
+                           MOE_FLAG_WEIGHTS_FP8_BLOCK128;
     if ((f & ~known) || ((f & MOE_FLAG_NARROW) && (f & MOE_FLAG_TILED)) ||
         ((f & MOE_FLAG_ONE_KERNEL) &&
          (f & (MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH | MOE_FLAG_DEBUG_SPIN_BOUND))))
         return MOE_EINVAL;
+    const bool w8 = (f & MOE_FLAG_WEIGHTS_FP8_BLOCK128) != 0;
+    if (w8 && (f & (MOE_FLAG_W13_PREINTERLEAVED | MOE_FLAG_W_SCALES_PER_ROW))) return MOE_EINVAL;
+    if (w8 && (f & (MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH | MOE_FLAG_ONE_KERNEL))) return MOE_EUNSUPPORTED;
     if ((f & MOE_FLAG_ONE_KERNEL) && !moe::layer_small_fits(d.T, d.topk)) return MOE_EUNSUPPORTED;
     if (!aligned16(a->x) || !aligned16(a->w13) || !aligned16(a->w2) || !aligned16(a->y) ||
         ((uintptr_t)a->w13_sf & 3) || ((uintptr_t)a->w2_sf & 3))
@@ -361,7 +376,8 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     rp.w_out = at<float>(ws, c.topk_w);
     rp.cnt = at<int>(ws, c.cnt);
     rp.slot_in_e = at<int32_t>(ws, c.slot_in_e);
-    rp.x = a->x;
+    // block-FP8 weights quantise x per 128 in a launch of their own
+    rp.x = w8 ? nullptr : a->x;
     rp.xq = at<uint8_t>(ws, c.xq);
     rp.xsf = at<uint8_t>(ws, c.xsf);
     rp.T = d.T;
@@ -422,6 +438,7 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     gp.w2 = a->w2;
     gp.w2sf = a->w2_sf;
     gp.o = at<uint16_t>(ws, c.o);
+    gp.hf32 = at<float>(ws, c.o);
     gp.T = d.T;
     gp.H = d.H;
     gp.I = d.I;
@@ -460,9 +477,23 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     // ONE_LAUNCH alone keeps its tiled meaning; with NARROW it fuses the narrow GEMMs
     if ((a->flags & MOE_FLAG_ONE_LAUNCH) && !(a->flags & MOE_FLAG_NARROW)) narrow = false;
     const bool fused = (a->flags & MOE_FLAG_ONE_LAUNCH) != 0;
-    if (ev) err = hipEventRecord(ev[1], s);
     hipEvent_t* kev = a->kernel_events;
     hipEvent_t k0 = kev ? kev[0] : nullptr, k1 = kev ? kev[1] : nullptr;
+    if (w8) {
+        // block-FP8 weights: x per 128 -> narrow GEMM1 (float32 h) -> h per 128 -> narrow GEMM2
+        err = moe::launch_quant_rows128(a->x, false, d.T, d.H, rp.xq, reinterpret_cast<float*>(rp.xsf), s);
+        if (err == hipSuccess && ev) err = hipEventRecord(ev[1], s);
+        if (err == hipSuccess) err = moe::launch_narrow_w8_gemm1(gp, s, k0, k1);
+        if (err == hipSuccess)
+            err = moe::launch_quant_rows128(gp.hf32, true, R, d.I, gp.hq, reinterpret_cast<float*>(gp.hsf), s);
+        if (err == hipSuccess && ev) err = hipEventRecord(ev[2], s);
+        if (err == hipSuccess) err = moe::launch_narrow_w8_gemm2(gp, s);
+        if (err == hipSuccess && ev) err = hipEventRecord(ev[3], s);
+        if (err == hipSuccess) err = moe::launch_combine(gp.o, sp.slot_of, d.T, d.topk, d.H, a->y, s);
+        if (err == hipSuccess && ev) err = hipEventRecord(ev[4], s);
+        return err == hipSuccess ? MOE_OK : hip_fail(err);
+    }
+    if (ev) err = hipEventRecord(ev[1], s);
     if (fused) {
         // GEMM1 -> SwiGLU -> GEMM2 in one launch: both events after it
         if (err == hipSuccess)

@@ -83,6 +83,7 @@ struct GemmParams {
     const uint8_t* w2;          // [E, H, I/2]
     const uint8_t* w2sf;        // [E, I/128, H, 4]
     uint16_t* o;                // [R, H]    GEMM2 output (BF16)
+    float* hf32;                // [R, I]    block-FP8 weights: GEMM1's h in float32 (shares o's bytes)
     int64_t T;
     int H, I, E, topk;
     int max_mtiles;             // upper bound of mtile_off[E]
@@ -156,6 +157,18 @@ hipError_t launch_narrow_gemm2(const GemmParams& p, hipStream_t s, hipEvent_t ev
                                hipEvent_t ev1 = nullptr);
 hipError_t launch_narrow_fused(const GemmParams& p, hipStream_t s, hipEvent_t ev0 = nullptr,
                                hipEvent_t ev1 = nullptr);
+// the narrow GEMMs with block-FP8 weights (GEMM1 leaves float32 h in p.hf32)
+hipError_t launch_narrow_w8_gemm1(const GemmParams& p, hipStream_t s, hipEvent_t ev0 = nullptr,
+                                  hipEvent_t ev1 = nullptr);
+hipError_t launch_narrow_w8_gemm2(const GemmParams& p, hipStream_t s, hipEvent_t ev0 = nullptr,
+                                  hipEvent_t ev1 = nullptr);
+// block-FP8 quantisers: rows of BF16 (f32_in false) or float32 values -> E4M3
+// codes [rows, cols] + float32 scales [cols/128][rows] (one per row per 128);
+// BF16 weights [rows, cols] -> E4M3 codes + float32 scales [rows/128][cols/128]
+hipError_t launch_quant_rows128(const void* src, bool f32_in, int64_t rows, int cols, uint8_t* q, float* sf,
+                                hipStream_t s);
+hipError_t launch_pack_block128(const uint16_t* w, int64_t rows, int cols, uint8_t* q, float* sf,
+                                hipStream_t s);
 
 // Read `bytes` (a multiple of 16) from src once, with nothing else to do (the
 // HBM read ceiling of a footprint); sink takes a flag no real data sets.

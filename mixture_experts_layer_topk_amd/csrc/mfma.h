@@ -20,6 +20,35 @@ MOE_DEV v4f mfma_fp8_fp4(const v8i& a, const v4i& b, const v4f& c, int sa, int s
                                                             sb);
 }
 
+// Block-FP8 weights: one 128-wide K block of a 16 x 16 tile, FP8 E4M3 A and B
+// (32 bytes per lane each, in the 16 x 16 x 128 instruction's operand layout)
+// widened to BF16 (exact: E4M3 has 3 mantissa bits) and multiplied by four
+// 16 x 16 x 32 BF16 MFMAs into zero accumulators; the caller applies the two
+// float32 block scales.  The FP8 instructions are not used here because they do
+// not sum in FP32: on gfx950 a 16 x 16 x 128 FP8 x FP8 product errs by up to
+// 2^-12.8 of sum |a b| over random E4M3 codes, the BF16 path by 2^-22.
+// Instruction s takes bytes [8 s, 8 s + 8) of every lane's 32 (K elements
+// 16 g + 8 s .. for s < 2, 64 + 16 g + 8 (s - 2) .. else); A and B use the same
+// mapping, so the four instructions sum every K of the block exactly once.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+MOE_DEV void fp8x32_to_bf16(const v8i& v, v8bf (&out)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2 * s], 1.0f, false);
+        const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2 * s], 1.0f, true);
+        const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2 * s + 1], 1.0f, false);
+        const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2 * s + 1], 1.0f, true);
+        out[s] = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    }
+}
+MOE_DEV v4f mfma_bf16_block(const v8bf (&a)[4], const v8bf (&b)[4]) {
+    v4f c = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], c, 0, 0, 0);
+    return c;
+}
+
 // silu(g) = g / (1 + e^-g), with the hardware exp2 and reciprocal (about one
 // ulp each; a large negative g gives e^-g = inf and silu = -0).
 MOE_DEV float silu(float g) {

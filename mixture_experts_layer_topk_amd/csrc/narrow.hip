@@ -51,6 +51,34 @@ hipError_t launch_narrow_gemm2(const GemmParams& p, hipStream_t s, hipEvent_t ev
     return launch_narrow<false>(p, s, ev0, ev1);
 }
 
+// Block-FP8 weights ("MonoMoe kernel — design", fixed-shape paragraph): the same
+// units and pipeline with FP8 weight operands and float32 block scales.
+template <bool kG1>
+__global__ __launch_bounds__(kNarrowThreads) void narrow_w8_gemm_kernel(GemmParams p) {
+    narrow_gemm<kG1, false, true>(p, blockIdx.x, gridDim.x);
+}
+
+template <bool kG1>
+static hipError_t launch_narrow_w8(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    int cus = 0;
+    hipError_t err = device_cus(&cus);
+    if (err != hipSuccess) return err;
+    const int nch = (kG1 ? p.I : p.H) / NarrowCfg<kG1, true>::kCols;
+    const int64_t units = (int64_t)p.max_subs * nch;
+    const int64_t grid = std::min<int64_t>(units, (int64_t)kNarrowBlocksPerCU * cus);
+    if (grid <= 0) return record_pair(ev0, ev1, s);
+    hipExtLaunchKernelGGL(narrow_w8_gemm_kernel<kG1>, dim3((unsigned)grid), dim3(kNarrowThreads), 0, s, ev0,
+                          ev1, 0, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_narrow_w8_gemm1(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    return launch_narrow_w8<true>(p, s, ev0, ev1);
+}
+hipError_t launch_narrow_w8_gemm2(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    return launch_narrow_w8<false>(p, s, ev0, ev1);
+}
+
 // GEMM1 -> SwiGLU -> GEMM2 of the narrow kernels in one launch: every
 // workgroup runs its GEMM1 units, then its GEMM2 units, whose activation loads
 // wait on per-sub-tile ready counters (zeroed by the bucketing stage of the

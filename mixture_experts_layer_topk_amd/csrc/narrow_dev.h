@@ -15,23 +15,26 @@ constexpr int kBatch = kNarrowThreads / kSubRows;   // unit headers fetched per 
 constexpr int kNarrowBlocksPerCU = 2;
 constexpr int kNarrowSpinLimit = 1 << 14;   // polls of a ready counter before giving up (~20 ms)
 
-template <bool kG1>
+template <bool kG1, bool kW8 = false>
 struct NarrowCfg {
     static constexpr int kCols = kG1 ? 32 : 64;         // I columns (GEMM1) or H columns
     // K steps per item and wave, items in flight per wave.  GEMM1 loads two
     // K steps per item, so the two 64-byte halves of a weight row's 128-byte
     // line are requested together (6% faster at the decode shape); GEMM2's
     // K = I is too short per wave for that (each wave has I / 512 steps).
-    static constexpr int KC = kG1 ? 2 : 1;
-    static constexpr int NBUF = kG1 ? 2 : 4;
+    // FP8 weights (kW8) fill a 128-byte line per K step and take twice the
+    // registers per item: one K step per item, three items in flight.
+    static constexpr int KC = kW8 ? 1 : (kG1 ? 2 : 1);
+    static constexpr int NBUF = kW8 ? 3 : (kG1 ? 2 : 4);
 };
 
-template <int KC>
+template <int KC, bool kW8>
 struct NarrowBuf {
-    v4i b[KC][kNT];
-    uint32_t sb[KC][kNT];
+    v4i b[KC][kNT];             // FP4: the lane's 16 bytes; FP8: its first 16 of 32
+    v4i b2[kW8 ? KC : 1][kNT];  // FP8: the lane's second 16 bytes (K + 64)
+    uint32_t sb[KC][kNT];       // FP4: the step's 4 UE8M0 bytes; FP8: the block's float32 scale
     v4i alo[KC], ahi[KC];
-    uint32_t sa[KC];
+    uint32_t sa[KC];            // MXFP8: the step's 4 UE8M0 bytes; block FP8: the float32 scale
 };
 
 // The GEMM of workgroup `bid` of `G` (any G >= 1: the units are dealt out
@@ -43,9 +46,18 @@ struct NarrowBuf {
 // complete and then adds each finished unit to ready[sub-tile]; a GEMM2 batch
 // issues its first weight loads, waits until ready[] counts every GEMM1 unit
 // of each of its sub-tiles and then reads h with device-coherent loads.
-template <bool kG1, bool kCoh = false>
+//
+// kW8: block-FP8 weights (E4M3 codes [E, N, K], one float32 scale per 128 x 128
+// block) and activations with one float32 scale per row per 128 K ("MonoMoe
+// kernel — design", fixed-shape paragraph).  Each K step's 16 x 16 partial
+// (mfma_bf16_block: the FP8 values widened to BF16) is added with the row's
+// activation scale times the block's weight scale.  GEMM1 then stores h = silu(g) * up * w in
+// float32 (p.hf32), to be quantised per 128 columns by the next launch (a
+// group spans four units of different workgroups).
+template <bool kG1, bool kCoh = false, bool kW8 = false>
 MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
-    using Cfg = NarrowCfg<kG1>;
+    static_assert(!(kCoh && kW8), "block-FP8 weights run as separate launches");
+    using Cfg = NarrowCfg<kG1, kW8>;
     constexpr int KC = Cfg::KC, NBUF = Cfg::NBUF;
     // partial accumulators, two buffers: unit j writes buffer j % 2, whose
     // previous readers (unit j - 2) finished before unit j - 1's barrier
@@ -99,24 +111,32 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
         // Weights (expert e, column chunk nc) and activations are issued apart:
         // the first items' weights go out as soon as their expert is known,
         // before the unit headers (rows, routing weights) are resolved.
-        auto issue_w = [&](NarrowBuf<KC>& bf, int q, int e, int nc) {
+        auto issue_w = [&](NarrowBuf<KC, kW8>& bf, int q, int e, int nc) {
             q = min(q, nitems - 1);
             const int c = q % nchunk;
-            const uint8_t* wq_e = wq + (int64_t)e * wrows * (K / 2) + lg * 16;
+            constexpr int kRow = kW8 ? 1 : 2;             // elements per byte of a weight row
+            const uint8_t* wq_e = wq + (int64_t)e * wrows * (K / kRow) + lg * 16;
             const uint8_t* wsf_e = wsf + (int64_t)e * wrows * (K / kGroup);
+            // block-FP8 scales [E][N/128][K/128] float32
+            const float* wsf8_e = reinterpret_cast<const float*>(wsf) + (int64_t)e * (wrows / 128) * nk;
 #pragma unroll
             for (int jj = 0; jj < KC; ++jj) {
                 const int ks = max(0, min(kb + c * KC + jj, min(ke, nk) - 1));
 #pragma unroll
                 for (int t = 0; t < kNT; ++t) {
                     const int br = brow(nc, t);
-                    bf.b[jj][t] = *reinterpret_cast<const v4i*>(wq_e + (int64_t)br * (K / 2) +
-                                                                ks * (kKStep / 2));
-                    bf.sb[jj][t] = *reinterpret_cast<const uint32_t*>(wsf_e + ks * w_ks + br * w_rs);
+                    const uint8_t* row = wq_e + (int64_t)br * (K / kRow) + ks * (kKStep / kRow);
+                    bf.b[jj][t] = *reinterpret_cast<const v4i*>(row);
+                    if constexpr (kW8) {
+                        bf.b2[jj][t] = *reinterpret_cast<const v4i*>(row + 64);
+                        bf.sb[jj][t] = __builtin_bit_cast(uint32_t, wsf8_e[(br / 128) * nk + ks]);
+                    } else {
+                        bf.sb[jj][t] = *reinterpret_cast<const uint32_t*>(wsf_e + ks * w_ks + br * w_rs);
+                    }
                 }
             }
         };
-        auto issue_a = [&](NarrowBuf<KC>& bf, int q) {
+        auto issue_a = [&](NarrowBuf<KC, kW8>& bf, int q) {
             q = min(q, nitems - 1);
             const int j = q / nchunk, c = q - j * nchunk;
             const int64_t arow = s_arow[j][l16];
@@ -142,7 +162,7 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
                 }
             }
         };
-        auto issue = [&](NarrowBuf<KC>& bf, int q) {
+        auto issue = [&](NarrowBuf<KC, kW8>& bf, int q) {
             const int j = min(q, nitems - 1) / nchunk;
             issue_w(bf, q, s_hdr[j][0], s_hdr[j][3]);
             issue_a(bf, q);
@@ -168,7 +188,7 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
             hw = p.slot_w[hpos];
         }
 
-        NarrowBuf<KC> buf[NBUF];
+        NarrowBuf<KC, kW8> buf[NBUF];
 #pragma unroll
         for (int q = 0; q < NBUF - 1; ++q) {
             const int u = u0 + (min(q, nitems - 1) / nchunk) * G;
@@ -229,11 +249,23 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         h[i] = swiglu_w(g[i], u[i], wr[i]);
-                        // max |h| over the row's 16 columns (bit patterns of
-                        // non-negative floats order like the values)
-                        const uint32_t m = row_max_u32(f2u(h[i]) & 0x7FFFFFFFu);
-                        if (l16 == 0) s_amax[wave][4 * lg + i] = u2f(m);
+                        if constexpr (!kW8) {
+                            // max |h| over the row's 16 columns (bit patterns of
+                            // non-negative floats order like the values)
+                            const uint32_t m = row_max_u32(f2u(h[i]) & 0x7FFFFFFFu);
+                            if (l16 == 0) s_amax[wave][4 * lg + i] = u2f(m);
+                        }
                     }
+                }
+                if constexpr (kW8) {
+                    // h in float32; its 128-column groups are quantised by the next launch
+                    if (wave < 2) {
+                        const int icol = nc * Cfg::kCols + wave * 16 + l16;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (4 * lg + i < valid) p.hf32[(int64_t)(p0 + 4 * lg + i) * p.I + icol] = h[i];
+                    }
+                    return;
                 }
                 // an E4M3 group is the unit's 32 I columns: both waves' maxima
                 __syncthreads();
@@ -276,7 +308,7 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
                 }
             }
         };
-        auto consume = [&](const NarrowBuf<KC>& bf, int q) {
+        auto consume = [&](const NarrowBuf<KC, kW8>& bf, int q) {
             const int j = q / nchunk, c = q - j * nchunk;
             if (c == 0) {
 #pragma unroll
@@ -287,11 +319,33 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
                 if (kb + c * KC + jj < ke) {
                     const v8i a = v8i{bf.alo[jj][0], bf.alo[jj][1], bf.alo[jj][2], bf.alo[jj][3],
                                       bf.ahi[jj][0], bf.ahi[jj][1], bf.ahi[jj][2], bf.ahi[jj][3]};
-                    // lane group lg supplies the scale of K group lg of the step
-                    const int sa = (int)(bf.sa[jj] >> (8 * lg));
+                    if constexpr (kW8) {
+                        // scales of this lane's result rows 4 lg + i: row r's sits in lane r
+                        const float sa_lane = __builtin_bit_cast(float, bf.sa[jj]);
+                        float sa_r[4];
 #pragma unroll
-                    for (int t = 0; t < kNT; ++t)
-                        acc[t] = mfma_fp8_fp4(a, bf.b[jj][t], acc[t], sa, (int)(bf.sb[jj][t] >> (8 * lg)));
+                        for (int i = 0; i < 4; ++i) sa_r[i] = __shfl(sa_lane, 4 * lg + i, 64);
+                        v8bf abf[4];
+                        fp8x32_to_bf16(a, abf);
+#pragma unroll
+                        for (int t = 0; t < kNT; ++t) {
+                            const v8i b8 = v8i{bf.b[jj][t][0], bf.b[jj][t][1], bf.b[jj][t][2], bf.b[jj][t][3],
+                                               bf.b2[jj][t][0], bf.b2[jj][t][1], bf.b2[jj][t][2],
+                                               bf.b2[jj][t][3]};
+                            v8bf bbf[4];
+                            fp8x32_to_bf16(b8, bbf);
+                            const v4f part = mfma_bf16_block(abf, bbf);
+                            const float sw = __builtin_bit_cast(float, bf.sb[jj][t]);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(part[i], sa_r[i] * sw, acc[t][i]);
+                        }
+                    } else {
+                        // lane group lg supplies the scale of K group lg of the step
+                        const int sa = (int)(bf.sa[jj] >> (8 * lg));
+#pragma unroll
+                        for (int t = 0; t < kNT; ++t)
+                            acc[t] = mfma_fp8_fp4(a, bf.b[jj][t], acc[t], sa, (int)(bf.sb[jj][t] >> (8 * lg)));
+                    }
                 }
             }
             if (c == nchunk - 1) epilogue(j);

@@ -9,6 +9,9 @@ Tolerances (floating point only; integer outputs are compared exactly):
           - at most 0.1 % of them differ;
           - a differing value is at most one E4M3 grid step from the reference,
             measured on the grid of the larger of the two group scales;
+          - (with block-FP8 weights, whose float32 scales move in their last
+            bits with each group's largest value, the codes are compared
+            instead, and the scales must agree to a relative 1e-4)
           - the only exception is a value whose own rounding error bound
             allows more: the GPU and the reference each round a dot product of
             K FP8 x FP4 products in FP32, in different orders, so each
@@ -179,22 +182,48 @@ def e4m3_position(v: np.ndarray, s: np.ndarray) -> np.ndarray:
     return np.sign(v) * pos
 
 
-def check_hq(hq_g, hsf_g, hq_r, hsf_r, max_frac=1e-3, bound=None, max_beyond=1e-4, label="hq"):
+def check_hq(hq_g, hsf_g, hq_r, hsf_r, max_frac=1e-3, bound=None, max_beyond=1e-4, label="hq",
+             block=32):
     """hq against the reference (see the module docstring).  bound(rows, cols)
     returns the accumulation-order bound of |h_gpu - h_ref| for those elements
-    (float64); without it no value may be more than one grid step away."""
-    a = C.dequantize_blocks(hq_g, hsf_g, "e4m3")
-    b = C.dequantize_blocks(hq_r, hsf_r, "e4m3")
-    diff = a != b
-    n = diff.size
+    (float64); without it no value may be more than one grid step away.
+
+    block=32: UE8M0 scale bytes per 32 elements, compared in value space (a scale
+    that flips by a factor 2 changes every code of its group).  block=128: float32
+    scales per 128 elements (block-FP8 weights): a scale is max|h| / 448, so it
+    moves in its last bits with the group's largest value, which moves every value
+    and no code; there the codes are compared (at most max_frac differ, each by one
+    code step unless its bound allows more) and the scales must agree to a relative
+    1e-4."""
+    n = hq_g.size
+    if block == 32:
+        a = C.dequantize_blocks(hq_g, hsf_g, "e4m3")
+        b = C.dequantize_blocks(hq_r, hsf_r, "e4m3")
+        sc_g, sc_r = C.e8m0_value(hsf_g), C.e8m0_value(hsf_r)
+        diff = a != b
+    else:
+        sc_g, sc_r = np.asarray(hsf_g, np.float64), np.asarray(hsf_r, np.float64)
+        rel = np.abs(sc_g - sc_r) / np.maximum(sc_r, 1e-300)
+        print(f"    {label}: float32 scales agree to a relative {rel.max():.2e} (limit 1e-4)", flush=True)
+        assert rel.max() <= 1e-4, f"scales differ by a relative {rel.max():.2e}"
+        a = C.E4M3_TABLE[hq_g.astype(np.int64)] * np.repeat(sc_g, block, -1)
+        b = C.E4M3_TABLE[hq_r.astype(np.int64)] * np.repeat(sc_r, block, -1)
+        diff = hq_g != hq_r
     nd = int(diff.sum())
     frac = nd / n if n else 0.0
     max_steps, beyond = 0.0, 0
     if nd:
-        s = np.maximum(np.repeat(C.e8m0_value(hsf_g), 32, -1), np.repeat(C.e8m0_value(hsf_r), 32, -1))
+        s = np.maximum(np.repeat(sc_g, block, -1), np.repeat(sc_r, block, -1))
         r, c = np.nonzero(diff)
         sd = s[r, c]
-        steps = np.abs(e4m3_position(a[r, c], sd) - e4m3_position(b[r, c], sd))
+        if block == 32:
+            steps = np.abs(e4m3_position(a[r, c], sd) - e4m3_position(b[r, c], sd))
+        else:
+            # code steps: the magnitude codes 0x00..0x7E are in value order
+            def signed(code):
+                code = code.astype(np.int64)
+                return np.where(code & 0x80, -(code & 0x7F), code & 0x7F)
+            steps = np.abs(signed(hq_g[r, c]) - signed(hq_r[r, c])).astype(np.float64)
         max_steps = float(steps.max())
         far = steps > 1.0 + 1e-9
         beyond = int(far.sum())
@@ -209,14 +238,15 @@ def check_hq(hq_g, hsf_g, hq_r, hsf_r, max_frac=1e-3, bound=None, max_beyond=1e-
             else:
                 lim = bound(rr, cc)
             bad = np.abs(a[rr, cc] - b[rr, cc]) > (lim + step) * (1 + 1e-9)
-            lines = [f"row {i} col {j}: gpu code {hq_g[i, j]:#04x} sf {hsf_g[i, j // 32]} = {a[i, j]:.6g}, "
-                     f"ref code {hq_r[i, j]:#04x} sf {hsf_r[i, j // 32]} = {b[i, j]:.6g}, "
+            lines = [f"row {i} col {j}: gpu code {hq_g[i, j]:#04x} sf {hsf_g[i, j // block]} = {a[i, j]:.6g}, "
+                     f"ref code {hq_r[i, j]:#04x} sf {hsf_r[i, j // block]} = {b[i, j]:.6g}, "
                      f"bound {l:.3g} + step {st:.3g}"
                      for i, j, l, st in list(zip(rr, cc, lim, step))[:12]]
             print(f"    {label}: {beyond} value(s) beyond one grid step:\n      " + "\n      ".join(lines),
                   flush=True)
             assert not bad.any(), f"{int(bad.sum())} hq values differ beyond their accumulation bound"
-    print(f"    {label}: {n} values, {nd} differ ({frac:.2e}, limit {max_frac:.0e}); largest distance "
+    what = "values" if block == 32 else "codes"
+    print(f"    {label}: {n} {what}, {nd} differ ({frac:.2e}, limit {max_frac:.0e}); largest distance "
           f"{max_steps:.3g} grid steps; {beyond} beyond one step (limit {max_beyond:.0e} of the values)",
           flush=True)
     assert frac <= max_frac, f"{frac:.2e} of hq differ"

@@ -75,9 +75,16 @@ def test_forward_rejects_null_and_small_workspace_without_gpu():
                       m.FLAG_ONE_KERNEL | m.FLAG_TILED, m.FLAG_ONE_KERNEL | m.FLAG_ONE_LAUNCH,
                       # the one-kernel layer's grid barriers guard the tables its phases index with
                       m.FLAG_ONE_KERNEL | m.FLAG_DEBUG_SPIN_BOUND,
-                      256, 1 << 31):                                           # unknown or conflicting
+                      # block-FP8 weights have their own scale layout and no gate/up interleave
+                      m.FLAG_WEIGHTS_FP8_BLOCK128 | m.FLAG_W13_PREINTERLEAVED,
+                      m.FLAG_WEIGHTS_FP8_BLOCK128 | m.FLAG_W_SCALES_PER_ROW,
+                      512, 1 << 31):                                           # unknown or conflicting
         a.flags = bad_flags
         assert m._lib.moe_forward(ctypes.byref(a), None) == m.MOE_EINVAL
+    # block-FP8 weights run on the narrow kernels in separate launches only
+    for bad_flags in (m.FLAG_TILED, m.FLAG_ONE_LAUNCH, m.FLAG_ONE_KERNEL):
+        a.flags = m.FLAG_WEIGHTS_FP8_BLOCK128 | bad_flags
+        assert m._lib.moe_forward(ctypes.byref(a), None) == m.MOE_EUNSUPPORTED
     # the one-kernel layer takes at most 1024 routed pairs
     big = m.dims(129, 256, 128, 32, 8)
     a.dims = big
@@ -89,6 +96,9 @@ def test_forward_rejects_null_and_small_workspace_without_gpu():
 def test_quant_and_pack_reject_bad_sizes():
     m = _lib()
     p = ctypes.c_void_p(1 << 20)
+    assert m._lib.moe_pack_weights_fp8_block128(p, 100, 128, p, p, None) == m.MOE_EINVAL   # rows % 128
+    assert m._lib.moe_pack_weights_fp8_block128(p, 128, 96, p, p, None) == m.MOE_EINVAL    # cols % 128
+    assert m._lib.moe_pack_weights_fp8_block128(p, 0, 128, p, p, None) == m.MOE_OK
     assert m._lib.moe_quant_act(p, 4, 48, p, p, None) == m.MOE_EINVAL
     assert m._lib.moe_pack_weights(p, 4, 0, p, p, None) == m.MOE_EINVAL
     assert m._lib.moe_quant_act(p, 0, 64, p, p, None) == m.MOE_OK            # empty is a no-op
