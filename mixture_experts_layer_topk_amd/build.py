@@ -15,6 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+PROBE = os.path.join(ROOT, "tests", "probes", "mfma_precision")
 SOURCES = ["api.hip", "route.hip", "quant.hip", "gemm.hip", "narrow.hip", "combine.hip", "layer.hip",
            "stream.hip", "block8.hip"]
 
@@ -54,6 +55,9 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    # the matrix-instruction accuracy measurement the parity bounds rest on (run by
+    # a GPU test; not part of the library)
+    _run([HIPCC, *FLAGS, os.path.join(ROOT, "tests", "probes", "mfma_precision.hip"), "-o", PROBE])
     return LIB
 
 

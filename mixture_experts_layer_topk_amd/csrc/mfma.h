@@ -26,7 +26,7 @@ MOE_DEV v4f mfma_fp8_fp4(const v8i& a, const v4i& b, const v4f& c, int sa, int s
 // 16 x 16 x 32 BF16 MFMAs into zero accumulators; the caller applies the two
 // float32 block scales.  The FP8 instructions are not used here because they do
 // not sum in FP32: on gfx950 a 16 x 16 x 128 FP8 x FP8 product errs by up to
-// 2^-12.8 of sum |a b| over random E4M3 codes, the BF16 path by 2^-22.
+// 2^-12.6 of sum |a b| over random E4M3 codes, the BF16 path by 2^-21.8.
 // Instruction s takes bytes [8 s, 8 s + 8) of every lane's 32 (K elements
 // 16 g + 8 s .. for s < 2, 64 + 16 g + 8 (s - 2) .. else); A and B use the same
 // mapping, so the four instructions sum every K of the block exactly once.

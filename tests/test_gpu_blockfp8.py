@@ -90,7 +90,8 @@ def _hq_bound(ref, pairs, layer, I):
             rows13 = B.dequant_weights(q13, s13)[[c, I + c]]
             K = a.size
             g, u = float(a @ rows13[0]), float(a @ rows13[1])
-            gamma = (K + 1) * u32 / (1 - (K + 1) * u32)
+            # each block's BF16 partial, then its scaling by two float32 factors
+            gamma = G.accumulation_rel(K, G.MFMA_BF16_REL + 2 * u32)
             dg = gamma * float(np.abs(a) @ np.abs(rows13[0]))
             du = gamma * float(np.abs(a) @ np.abs(rows13[1]))
             silu = g / (1.0 + np.exp(-g)) if g > -700 else 0.0
