@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--weights", choices=("fp4", "fp8-block128"), default="fp4",
                     help="weight format: FP4 E2M1 + UE8M0/32 (the layer's), or the block-FP8 "
                          "variant (E4M3, one float32 scale per 128 x 128 block; narrow GEMMs)")
+    ap.add_argument("--layout", choices=("staged", "canonical"), default="staged",
+                    help="FP4 weight-code layout moe_forward reads: staged (moe_stage_weights, "
+                         "one contiguous KiB per load) or canonical row-major")
     ap.add_argument("--gemm-path", choices=("auto", "narrow", "narrow-one-launch", "tiled", "one-launch",
                                             "one-kernel"),
                     default="auto", help="GEMM kernels moe_forward uses (default: its own choice)")
@@ -100,7 +103,7 @@ class Hip:
         return ms.value
 
 
-def setup_device(w, m, torch, fmt="fp4"):
+def setup_device(w, m, torch, fmt="fp4", layout="staged"):
     import moe_workloads as W
     from concurrent.futures import ThreadPoolExecutor
 
@@ -132,6 +135,8 @@ def setup_device(w, m, torch, fmt="fp4"):
             w2q[e], w2sf[e] = pack(up(b2))
     if not fp8:
         w13sf, w2sf = m.scales_kmajor(w13sf, w.H), m.scales_kmajor(w2sf, w.I)
+        if layout == "staged":
+            w13q, w2q = m.stage_weights(w13q, True), m.stage_weights(w2q, False)
     torch.cuda.synchronize()
     return x, logits, w13q, w13sf, w2q, w2sf
 
@@ -337,7 +342,9 @@ def main():
         w = replace(w.with_tokens(a.tokens), name=f"{w.name}_T{a.tokens}")
     if a.flush_mb is None:
         a.flush_mb = 1024 if w.name in HBM_BOUND else 0
-    x, logits, w13q, w13sf, w2q, w2sf = setup_device(w, m, torch, a.weights)
+    if a.weights != "fp4":
+        a.layout = "canonical"
+    x, logits, w13q, w13sf, w2q, w2sf = setup_device(w, m, torch, a.weights, a.layout)
     d = m.dims(w.T, w.H, w.I, w.E, w.topk, w.score_fn, w.renorm)
     ws = m.new_workspace(d)
     y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
@@ -355,6 +362,8 @@ def main():
              "narrow-one-launch": m.FLAG_NARROW | m.FLAG_ONE_LAUNCH}[a.gemm_path]
     if a.weights == "fp8-block128":
         flags |= m.FLAG_WEIGHTS_FP8_BLOCK128
+    if a.layout == "staged":
+        flags |= m.FLAG_W_STAGED
     args_plain = m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, flags=flags)
     args_ev = [m.forward_args(d, x, w13q, w13sf, w2q, w2sf, y, ws, logits=logits, flags=flags,
                               stage_events=e, kernel_events=kev[i] if kev else None)
@@ -428,7 +437,8 @@ def main():
         "data": "synthetic (seeded N(0,1) x and logits, N(0,0.02) BF16 weights quantised on the GPU)",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "topk": w.topk,
                    "score_fn": "sigmoid" if w.score_fn else "softmax", "renorm": bool(w.renorm),
-                   "zipf_s": w.zipf_s, "weights": a.weights, "parallelism": "single GPU"},
+                   "zipf_s": w.zipf_s, "weights": a.weights, "weight_layout": a.layout,
+                   "parallelism": "single GPU"},
         "layer_tflops": round(layer_tflops, 2),
         "layer_frac_mfma": round(layer_tflops / PEAK_MFMA_FP8_TFLOPS, 4),
         "stages_ms": {n: round(float(v), 4) for n, v in zip(m.STAGES, stage_ms)},

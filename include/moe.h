@@ -142,6 +142,13 @@ typedef struct moe_dims {
  * MOE_EUNSUPPORTED with TILED, ONE_LAUNCH or ONE_KERNEL; MOE_EINVAL with
  * W13_PREINTERLEAVED or W_SCALES_PER_ROW. */
 #define MOE_FLAG_WEIGHTS_FP8_BLOCK128 256u
+/* Staged FP4 weight codes ("MegaMoE：把通信和计算融合到一个 Mega Kernel", Python API
+ * walk-through: a one-time transform of the weights before the per-batch
+ * calls): w13 and w2 hold the codes as moe_stage_weights writes them; the
+ * scales keep the layout the other flags select.  Results are bit-identical to
+ * the canonical layout's.  MOE_EINVAL with W13_PREINTERLEAVED (the staged
+ * layout is made from the canonical one) or WEIGHTS_FP8_BLOCK128. */
+#define MOE_FLAG_W_STAGED 512u
 
 #define MOE_NUM_STAGE_EVENTS 5
 
@@ -150,7 +157,8 @@ typedef struct moe_dims {
  *   logits    device, float32 [T, E] router logits; or NULL, and then
  *   topk_idx  device, int32 [T, topk] expert ids (entries < 0 are skipped) and
  *   topk_w    device, float32 [T, topk] routing weights
- *   w13       device, FP4 [E, 2I, H/2]: rows [0, I) gate (W1), [I, 2I) up (W3)
+ *   w13       device, FP4 [E, 2I, H/2]: rows [0, I) gate (W1), [I, 2I) up (W3);
+ *             the staged layout (moe_stage_weights) with MOE_FLAG_W_STAGED, as w2
  *   w13_sf    device, UE8M0 [E, H/128, 2I, 4]: K-step major (moe_scales_kmajor
  *             of the per-row [E, 2I, H/32] scales); per-row [E, 2I, H/32]
  *             with MOE_FLAG_W_SCALES_PER_ROW
@@ -307,6 +315,24 @@ int moe_pack_weights_fp8_block128(const uint16_t* w, int64_t rows, int32_t cols,
  *   cols  K, a multiple of 128
  *   out   device uint8 [mats, cols/128, rows, 4]; must not overlap sf */
 int moe_scales_kmajor(const uint8_t* sf, int64_t mats, int32_t rows, int32_t cols, uint8_t* out,
+                      hipStream_t s);
+
+/* Weight-code layout change for moe_forward with MOE_FLAG_W_STAGED (a
+ * one-time weight transform, as the scale layout change above; "MegaMoE" study
+ * notes, "原始权重布局", for the canonical gate-then-up row order it starts
+ * from).  Each matrix's packed codes are regrouped so that the GEMMs' weight
+ * loads read whole contiguous KiB: rows in groups of 16, and the 64 bytes of K
+ * step ks (128 values) of row c of group g at byte (g * cols/128 + ks) * 1024 +
+ * 64 c of the matrix.  Group g = 8 b + n holds
+ *   W13 (is_w13 != 0, rows = 2I): projection n & 1 (0 gate, 1 up) of I column
+ *       64 b + 4 c + n / 2, i.e. canonical row (n & 1) * I + 64 b + 4 c + n / 2;
+ *   W2  (is_w13 == 0, rows = H):  canonical row 128 b + 8 c + n.
+ *   w     device uint8 [mats, rows, cols/2], canonical row order (moe_pack_weights)
+ *   rows  2I (W13) or H (W2), a multiple of 128
+ *   cols  K (H for W13, I for W2), a multiple of 128
+ *   out   device uint8, mats * rows * cols/2 bytes; must not overlap w
+ * MOE_EINVAL for bad sizes or pointers (w and out 16-byte aligned). */
+int moe_stage_weights(const uint8_t* w, int64_t mats, int32_t rows, int32_t cols, int32_t is_w13, uint8_t* out,
                       hipStream_t s);
 
 /* The whole layer ("MegaMoE" study notes, "Dispatch阶段" flow chart: route or

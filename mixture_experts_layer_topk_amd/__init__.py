@@ -23,6 +23,7 @@ FLAG_NONE, FLAG_NARROW, FLAG_TILED, FLAG_ONE_LAUNCH, FLAG_ONE_KERNEL = 0, 1, 2, 
 FLAG_W13_PREINTERLEAVED, FLAG_W_SCALES_PER_ROW = 16, 32
 FLAG_KEEP_INTERMEDIATES, FLAG_DEBUG_SPIN_BOUND = 64, 128
 FLAG_WEIGHTS_FP8_BLOCK128 = 256
+FLAG_W_STAGED = 512
 
 
 class MoeError(RuntimeError):
@@ -58,7 +59,7 @@ class Layout(ctypes.Structure):
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_workspace_size", "moe_workspace_layout", "moe_workspace_init", "moe_route",
            "moe_route_noalloc", "moe_quant_act", "moe_pack_weights", "moe_pack_weights_fp8_block128",
-           "moe_scales_kmajor", "moe_forward",
+           "moe_scales_kmajor", "moe_stage_weights", "moe_forward",
            "moe_check_status", "moe_stream_read", "moe_error_string")
 
 
@@ -77,6 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_pack_weights.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_pack_weights_fp8_block128.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_scales_kmajor.argtypes = [vp, i64, i32, i32, vp, vp]
+    lib.moe_stage_weights.argtypes = [vp, i64, i32, i32, i32, vp, vp]
     lib.moe_forward.argtypes = [ctypes.POINTER(Args), vp]
     lib.moe_check_status.argtypes = [vp, vp]
     lib.moe_stream_read.argtypes = [vp, sz, vp, vp, vp, vp]
@@ -172,6 +174,16 @@ def scales_kmajor(sf: torch.Tensor, cols: int) -> torch.Tensor:
     mats = sf.numel() // (rows * (cols // 32))
     out = torch.empty(sf.shape[:-2] + (cols // 128, rows, 4), dtype=torch.uint8, device=sf.device)
     _check(_lib.moe_scales_kmajor(_ptr(sf), mats, rows, cols, _ptr(out), _stream()))
+    return out
+
+
+def stage_weights(w: torch.Tensor, is_w13: bool) -> torch.Tensor:
+    """Packed FP4 codes [..., rows, K/2] in canonical row order (W13: gate rows, then
+    up rows) -> the staged layout moe_forward reads with FLAG_W_STAGED (same size)."""
+    rows, cols = w.shape[-2], 2 * w.shape[-1]
+    mats = w.numel() // (rows * (cols // 2))
+    out = torch.empty_like(w)
+    _check(_lib.moe_stage_weights(_ptr(w), mats, rows, cols, 1 if is_w13 else 0, _ptr(out), _stream()))
     return out
 
 

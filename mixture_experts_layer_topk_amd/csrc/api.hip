@@ -340,6 +340,18 @@ int moe_scales_kmajor(const uint8_t* sf, int64_t mats, int32_t rows, int32_t col
     return err == hipSuccess ? MOE_OK : hip_fail(err);
 }
 
+int moe_stage_weights(const uint8_t* w, int64_t mats, int32_t rows, int32_t cols, int32_t is_w13, uint8_t* out,
+                      hipStream_t s) {
+    if (mats < 0 || rows < 0 || cols <= 0 || cols % 128 != 0 || rows % 128 != 0) return MOE_EINVAL;
+    if (mats == 0 || rows == 0) return MOE_OK;
+    const uint64_t bytes = (uint64_t)mats * (uint64_t)rows * (uint64_t)(cols / 2);
+    if (!w || !out || !aligned16(w) || !aligned16(out)) return MOE_EINVAL;
+    const uintptr_t a0 = (uintptr_t)w, b0 = (uintptr_t)out;
+    if (a0 < b0 + bytes && b0 < a0 + bytes) return MOE_EINVAL;
+    hipError_t err = moe::launch_stage_weights(w, mats, rows, cols, is_w13 != 0, out, s);
+    return err == hipSuccess ? MOE_OK : hip_fail(err);
+}
+
 int moe_forward(const moe_args_t* a, hipStream_t s) {
     if (!a) return MOE_EINVAL;
     const moe_dims_t& d = a->dims;
@@ -352,13 +364,15 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     const uint32_t known = MOE_FLAG_NARROW | MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH | MOE_FLAG_ONE_KERNEL |
                            MOE_FLAG_W13_PREINTERLEAVED | MOE_FLAG_W_SCALES_PER_ROW |
                            MOE_FLAG_KEEP_INTERMEDIATES | MOE_FLAG_DEBUG_SPIN_BOUND |
-                           MOE_FLAG_WEIGHTS_FP8_BLOCK128;
+                           MOE_FLAG_WEIGHTS_FP8_BLOCK128 | MOE_FLAG_W_STAGED;
     if ((f & ~known) || ((f & MOE_FLAG_NARROW) && (f & MOE_FLAG_TILED)) ||
         ((f & MOE_FLAG_ONE_KERNEL) &&
          (f & (MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH | MOE_FLAG_DEBUG_SPIN_BOUND))))
         return MOE_EINVAL;
     const bool w8 = (f & MOE_FLAG_WEIGHTS_FP8_BLOCK128) != 0;
-    if (w8 && (f & (MOE_FLAG_W13_PREINTERLEAVED | MOE_FLAG_W_SCALES_PER_ROW))) return MOE_EINVAL;
+    if (w8 && (f & (MOE_FLAG_W13_PREINTERLEAVED | MOE_FLAG_W_SCALES_PER_ROW | MOE_FLAG_W_STAGED)))
+        return MOE_EINVAL;
+    if ((f & MOE_FLAG_W_STAGED) && (f & MOE_FLAG_W13_PREINTERLEAVED)) return MOE_EINVAL;
     if (w8 && (f & (MOE_FLAG_TILED | MOE_FLAG_ONE_LAUNCH | MOE_FLAG_ONE_KERNEL))) return MOE_EUNSUPPORTED;
     if ((f & MOE_FLAG_ONE_KERNEL) && !moe::layer_small_fits(d.T, d.topk)) return MOE_EUNSUPPORTED;
     if (!aligned16(a->x) || !aligned16(a->w13) || !aligned16(a->w2) || !aligned16(a->y) ||
@@ -447,6 +461,7 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
     // a bounded wait that gives up after one failed poll (DEBUG_SPIN_BOUND), else the kernels' own
     gp.spin_limit = (f & MOE_FLAG_DEBUG_SPIN_BOUND) ? 1 : 0;
     gp.w13_il = (f & MOE_FLAG_W13_PREINTERLEAVED) ? 1 : 0;
+    gp.w_staged = (f & MOE_FLAG_W_STAGED) ? 1 : 0;
     if (f & MOE_FLAG_W_SCALES_PER_ROW) {        // [E, rows, K/32]
         gp.w13sf_rs = d.H / 32;
         gp.w2sf_rs = d.I / 32;

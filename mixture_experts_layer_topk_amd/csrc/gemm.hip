@@ -194,7 +194,11 @@ MOE_DEV void load_lds4(const void* g, uint8_t* lds) {
 // an XCD's own L2, while the weights keep the cached path.
 // kIL: W13 is in the gran-8 gate/up row interleave (a compile-time choice: a
 // run-time select in the row mapping costs the GEMM1 kernel register spills).
-template <int BM, int BN, int WM, int WN, bool kG1, bool kCoh, bool kIL = false>
+// kST: the weight codes are in the staged layout (16-row groups in the order
+// the B tile stages them, one contiguous KiB per group and K step), so every
+// B load instruction reads one KiB instead of 16 row pieces of 64 bytes; the
+// weight scales keep the canonical row order.
+template <int BM, int BN, int WM, int WN, bool kG1, bool kCoh, bool kIL = false, bool kST = false>
 struct TileEngine {
     using C = Cfg<BM, BN, WM, WN, kG1>;
     static constexpr int kAuxA = (kCoh && !kG1) ? kCohAux : 0;
@@ -352,7 +356,19 @@ struct TileEngine {
         for (int j = 0; j < C::kBI; ++j) {
             const int n = 16 * (j * C::kWaves + L.wave) + (L.lane >> 2);
             const int c = (L.lane & 3) ^ b_swz(n);
-            b_src[j] = b_row(n) * (uint32_t)b_stride + c * 16;
+            if constexpr (kST) {
+                // LDS rows 16 gi .. 16 gi + 15 are MFMA column tile gi % NT of wave
+                // slice gi / NT: staged group 8 b + nt of the expert, b the slice's
+                // column block (the last one for a partial n-tile: never stored)
+                static_assert(C::NT == 8 && C::WTN / (kG1 ? 2 : 1) == (kG1 ? 64 : 128),
+                              "staged groups are the wave slices' column tiles");
+                const int gi = j * C::kWaves + L.wave;
+                const int blk = min(ntile * WN + gi / C::NT, (kG1 ? p.I / 64 : p.H / 128) - 1);
+                const int g = 8 * blk + gi % C::NT;
+                b_src[j] = (uint32_t)(g * nk) * (uint32_t)kStagedBlock + (L.lane >> 2) * 64 + c * 16;
+            } else {
+                b_src[j] = b_row(n) * (uint32_t)b_stride + c * 16;
+            }
         }
         // scale blocks of a late wave (an early wave's values are not used)
         const int ew = L.wave % C::kEarly;
@@ -393,7 +409,7 @@ struct TileEngine {
                 load_lds4<0>(ld_sw + sb_src[j], sSB + (C::kSBE * ew + j) * 256);
         }
         ld_a += BK;
-        ld_w += BK / 2;
+        ld_w += kST ? kStagedBlock : BK / 2;
         ld_sa += sa_slab;
         ld_sw += sb_ks;
     }
@@ -609,9 +625,9 @@ struct TileEngine {
 };
 
 // One tile, loaded, computed and stored on its own (the one-launch kernel).
-template <int BM, int BN, int WM, int WN, bool kG1, bool kCoh, bool kIL>
+template <int BM, int BN, int WM, int WN, bool kG1, bool kCoh, bool kIL, bool kST>
 MOE_DEV void gemm_tile(const GemmParams& p, int mt, int ntile, uint8_t* smem) {
-    TileEngine<BM, BN, WM, WN, kG1, kCoh, kIL> eng(p, smem);
+    TileEngine<BM, BN, WM, WN, kG1, kCoh, kIL, kST> eng(p, smem);
     const int4 rec = p.mtile_rec[mt];        // {expert, first position, rows}
     eng.load_rows_now(rec, 0);
     eng.set_tile(rec, ntile, 0);
@@ -649,10 +665,10 @@ MOE_DEV int xcd_slot() { return sched::tile_slot(blockIdx.x, gridDim.x); }
 // sources set up (step nk - 2), and the last two steps issue the next tile's
 // first two K steps instead of reloading the current tile's last one, so the
 // epilogue overlaps those loads and the next tile starts on a full pipeline.
-template <int BM, int BN, int WM, int WN, bool kG1, bool kIL>
+template <int BM, int BN, int WM, int WN, bool kG1, bool kIL, bool kST>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    using Eng = TileEngine<BM, BN, WM, WN, kG1, false, kIL>;
+    using Eng = TileEngine<BM, BN, WM, WN, kG1, false, kIL, kST>;
     const int NT = gemm_ntiles<BN>(p, kG1);
     const int mtiles = p.mtile_off[p.E];
     const int total = mtiles * NT;
@@ -723,7 +739,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
 // entries earlier in the list and every workgroup is resident (one per CU),
 // so the waits always end; a wait longer than kSpinLimit polls stops, sets
 // *p.status and lets the tile run (its output is then wrong, never a hang).
-template <int BM, int BN, int WM, int WN, bool kIL>
+template <int BM, int BN, int WM, int WN, bool kIL, bool kST>
 __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     const int tid = threadIdx.x;
@@ -738,7 +754,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams 
         int mt, ntile;
         cur.tile(tile, NT1, NT2, &mt, &ntile);
         if (cur.sg.g1) {
-            gemm_tile<BM, BN, WM, WN, true, true, kIL>(p, mt, ntile, smem);
+            gemm_tile<BM, BN, WM, WN, true, true, kIL, kST>(p, mt, ntile, smem);
             // every thread's coherent h stores have completed (vmcnt(0)) before the barrier
             __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8) | (0 << 14));
             __syncthreads();
@@ -757,7 +773,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams 
                 }
             }
             __syncthreads();
-            gemm_tile<BM, BN, WM, WN, false, true, false>(p, mt, ntile, smem);
+            gemm_tile<BM, BN, WM, WN, false, true, false, kST>(p, mt, ntile, smem);
         }
     }
 }
@@ -781,10 +797,10 @@ static hipError_t allow_lds(const void* kern, int bytes, DeviceCache& done) {
     }, &ok);
 }
 
-template <bool kG1, bool kIL>
+template <bool kG1, bool kIL, bool kST>
 static hipError_t launch_gemm(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     using C = Cfg<kBM, kBN, kWM, kWN, kG1>;
-    auto kern = grouped_gemm_kernel<kBM, kBN, kWM, kWN, kG1, kIL>;
+    auto kern = grouped_gemm_kernel<kBM, kBN, kWM, kWN, kG1, kIL, kST>;
     const size_t lds = (size_t)C::kLds;
     static DeviceCache lds_set;
     hipError_t err = allow_lds((const void*)kern, (int)lds, lds_set);
@@ -800,16 +816,17 @@ static hipError_t launch_gemm(const GemmParams& p, hipStream_t s, hipEvent_t ev0
 }
 
 hipError_t launch_gemm1(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    return p.w13_il ? launch_gemm<true, true>(p, s, ev0, ev1) : launch_gemm<true, false>(p, s, ev0, ev1);
+    if (p.w_staged) return launch_gemm<true, false, true>(p, s, ev0, ev1);
+    return p.w13_il ? launch_gemm<true, true, false>(p, s, ev0, ev1) : launch_gemm<true, false, false>(p, s, ev0, ev1);
 }
 hipError_t launch_gemm2(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    return launch_gemm<false, false>(p, s, ev0, ev1);
+    return p.w_staged ? launch_gemm<false, false, true>(p, s, ev0, ev1) : launch_gemm<false, false, false>(p, s, ev0, ev1);
 }
 
-template <bool kIL>
+template <bool kIL, bool kST>
 static hipError_t launch_fused(const GemmParams& p_in, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     using C = Cfg<kBM, kBN, kWM, kWN, true>;
-    auto kern = fused_gemm_kernel<kBM, kBN, kWM, kWN, kIL>;
+    auto kern = fused_gemm_kernel<kBM, kBN, kWM, kWN, kIL, kST>;
     const size_t lds = (size_t)C::kLds;
     static DeviceCache lds_set;
     hipError_t err = allow_lds((const void*)kern, (int)lds, lds_set);
@@ -829,7 +846,8 @@ static hipError_t launch_fused(const GemmParams& p_in, hipStream_t s, hipEvent_t
 }
 
 hipError_t launch_fused_gemm(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    return p.w13_il ? launch_fused<true>(p, s, ev0, ev1) : launch_fused<false>(p, s, ev0, ev1);
+    if (p.w_staged) return launch_fused<false, true>(p, s, ev0, ev1);
+    return p.w13_il ? launch_fused<true, false>(p, s, ev0, ev1) : launch_fused<false, false>(p, s, ev0, ev1);
 }
 
 }  // namespace moe

@@ -61,6 +61,10 @@ hipError_t launch_pack_weights(const uint16_t* w, int64_t rows, int cols, uint8_
                                uint8_t* sf, hipStream_t s);
 hipError_t launch_scales_kmajor(const uint8_t* sf, int64_t mats, int rows, int cols, uint8_t* out,
                                 hipStream_t s);
+// packed FP4 codes [mats, rows, cols/2] (canonical row order) -> the staged layout
+// (w13: W13 with rows = 2I, else W2)
+hipError_t launch_stage_weights(const uint8_t* w, int64_t mats, int rows, int cols, bool w13, uint8_t* out,
+                                hipStream_t s);
 
 // Grouped GEMMs.  Positions p index the per-expert segments produced by the
 // bucketisation: expert e owns p in [offsets[e], offsets[e+1]).
@@ -98,6 +102,7 @@ struct GemmParams {
                                 // kernel's own bound (about 0.5 s)
     int w13_il;                 // W13 rows pre-interleaved: 8 gate rows, then the same 8
                                 // columns' up rows (else all gate rows, then all up rows)
+    int w_staged;               // W13 and W2 codes in the staged layout (canonical scales)
     // byte strides of the weight scales per weight row and per 128-wide K step:
     // K-step major (4, 4 * rows) or per row (K / 32, 4)
     int64_t w13sf_rs, w13sf_ks, w2sf_rs, w2sf_ks;

@@ -66,6 +66,7 @@ MOE_DEV void combine_phase(const GemmParams& gp, const int32_t* slot_of, uint16_
     }
 }
 
+template <bool kST>
 __global__ __launch_bounds__(kLayerThreads) void layer_small_kernel(RouteParams rp, ScatterParams sp,
                                                                     GemmParams gp, LayerParams lp) {
     const int G = gridDim.x, bid = blockIdx.x;
@@ -73,9 +74,9 @@ __global__ __launch_bounds__(kLayerThreads) void layer_small_kernel(RouteParams 
     if (bid == 0) bucket_small<kLayerThreads>(rp, sp, lp.npl);
     if (rp.x && (bid > 0 || G == 1)) quant_rows<kLayerThreads>(rp, G > 1 ? bid - 1 : 0, G > 1 ? G - 1 : 1);
     grid_barrier(lp.count, (unsigned)G, lp.status);
-    narrow_gemm<true>(gp, bid, G);
+    narrow_gemm<true, false, false, kST>(gp, bid, G);
     grid_barrier(lp.count, 2u * G, lp.status);
-    narrow_gemm<false>(gp, bid, G);
+    narrow_gemm<false, false, false, kST>(gp, bid, G);
     grid_barrier(lp.count, 3u * G, lp.status);
     switch (gp.topk) {   // 1 <= topk <= 16
         case 1: combine_phase<1>(gp, sp.slot_of, lp.y, bid, G); break;
@@ -111,12 +112,13 @@ bool layer_small_fits(int64_t T, int topk) { return T > 0 && T * topk <= kSmallP
 
 hipError_t launch_layer_small(const RouteParams& rp, const ScatterParams& sp, const GemmParams& gp,
                               LayerParams lp, hipStream_t s) {
-    static DeviceCache occupancy;
+    static DeviceCache occupancy[2];
     int cus = 0, per_cu = 0;
+    const void* kern = gp.w_staged ? (const void*)layer_small_kernel<true> : (const void*)layer_small_kernel<false>;
     hipError_t err = device_cus(&cus);
     if (err == hipSuccess)
-        err = per_device(occupancy, [](int, int* v) {
-            return hipOccupancyMaxActiveBlocksPerMultiprocessor(v, layer_small_kernel, kLayerThreads, 0);
+        err = per_device(occupancy[gp.w_staged ? 1 : 0], [&](int, int* v) {
+            return hipOccupancyMaxActiveBlocksPerMultiprocessor(v, kern, kLayerThreads, 0);
         }, &per_cu);
     if (err != hipSuccess) return err;
     if (per_cu < 1) return hipErrorInvalidConfiguration;
@@ -127,8 +129,7 @@ hipError_t launch_layer_small(const RouteParams& rp, const ScatterParams& sp, co
     ScatterParams b = sp;
     GemmParams c = gp;
     void* args[] = {&a, &b, &c, &lp};
-    return hipLaunchCooperativeKernel((const void*)layer_small_kernel, dim3(grid), dim3(kLayerThreads),
-                                      args, 0, s);
+    return hipLaunchCooperativeKernel(kern, dim3(grid), dim3(kLayerThreads), args, 0, s);
 }
 
 }  // namespace moe

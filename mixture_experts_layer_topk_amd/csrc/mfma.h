@@ -65,6 +65,21 @@ MOE_DEV int w13_row(int icol, int up, int I, int il) {
     return il ? ((icol >> 3) << 4) + (up << 3) + (icol & 7) : up * I + icol;
 }
 
+// Staged FP4 weight layout: the packed codes of one expert's matrix (N rows of
+// K E2M1 values, K / 2 bytes per row) regrouped so that every global->LDS load
+// of the tiled GEMM reads one contiguous KiB.  Rows are taken in groups of 16;
+// the 64 bytes of K step ks (128 values) of row c of group g sit at byte
+// (g * K / 128 + ks) * 1024 + 64 c.  Group g = 8 b + nt holds the 16 rows that
+// one MFMA column tile nt of the tiled kernel's wave slice b stages:
+//   W13 (N = 2I, slices of 64 I columns): projection nt & 1 (0 gate, 1 up)
+//        of I column 64 b + 4 c + nt / 2;
+//   W2  (N = H, slices of 128 H columns): output column 128 b + 8 c + nt.
+// The weight scales keep their own layout (canonical row order).
+constexpr int kStagedRows = 16;         // rows per group
+constexpr int kStagedBlock = 1024;      // bytes of one group for one K step
+MOE_DEV int staged_w13_row(int g, int c, int I) { return (g & 1) * I + 64 * (g >> 3) + 4 * c + ((g & 7) >> 1); }
+MOE_DEV int staged_w2_row(int g, int c) { return 128 * (g >> 3) + 8 * c + (g & 7); }
+
 // GEMM1 epilogue value of one element: silu(gate) * up * routing weight.
 MOE_DEV float swiglu_w(float g, float u, float w) { return silu(g) * u * w; }
 

@@ -25,9 +25,9 @@
 
 namespace moe {
 
-template <bool kG1>
+template <bool kG1, bool kST>
 __global__ __launch_bounds__(kNarrowThreads) void narrow_gemm_kernel(GemmParams p) {
-    narrow_gemm<kG1>(p, blockIdx.x, gridDim.x);
+    narrow_gemm<kG1, false, false, kST>(p, blockIdx.x, gridDim.x);
 }
 
 template <bool kG1>
@@ -39,8 +39,8 @@ static hipError_t launch_narrow(const GemmParams& p, hipStream_t s, hipEvent_t e
     const int64_t units = (int64_t)p.max_subs * nch;
     const int64_t grid = std::min<int64_t>(units, (int64_t)kNarrowBlocksPerCU * cus);
     if (grid <= 0) return record_pair(ev0, ev1, s);
-    hipExtLaunchKernelGGL(narrow_gemm_kernel<kG1>, dim3((unsigned)grid), dim3(kNarrowThreads), 0, s,
-                          ev0, ev1, 0, p);
+    auto kern = p.w_staged ? narrow_gemm_kernel<kG1, true> : narrow_gemm_kernel<kG1, false>;
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kNarrowThreads), 0, s, ev0, ev1, 0, p);
     return hipGetLastError();
 }
 
@@ -87,18 +87,20 @@ hipError_t launch_narrow_w8_gemm2(const GemmParams& p, hipStream_t s, hipEvent_t
 // is capped at the number of workgroups the GPU holds at once.  A wait longer
 // than kNarrowSpinLimit polls sets *p.status and gives up (wrong output, never
 // a hang).
+template <bool kST>
 __global__ __launch_bounds__(kNarrowThreads) void narrow_fused_kernel(GemmParams p) {
-    narrow_gemm<true, true>(p, blockIdx.x, gridDim.x);
-    narrow_gemm<false, true>(p, blockIdx.x, gridDim.x);
+    narrow_gemm<true, true, false, kST>(p, blockIdx.x, gridDim.x);
+    narrow_gemm<false, true, false, kST>(p, blockIdx.x, gridDim.x);
 }
 
 hipError_t launch_narrow_fused(const GemmParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    static DeviceCache occupancy;
+    static DeviceCache occupancy[2];
     int cus = 0, per_cu = 0;
+    auto kern = p.w_staged ? narrow_fused_kernel<true> : narrow_fused_kernel<false>;
     hipError_t err = device_cus(&cus);
     if (err == hipSuccess)
-        err = per_device(occupancy, [](int, int* v) {
-            return hipOccupancyMaxActiveBlocksPerMultiprocessor(v, narrow_fused_kernel, kNarrowThreads, 0);
+        err = per_device(occupancy[p.w_staged ? 1 : 0], [&](int, int* v) {
+            return hipOccupancyMaxActiveBlocksPerMultiprocessor(v, kern, kNarrowThreads, 0);
         }, &per_cu);
     if (err != hipSuccess) return err;
     per_cu = std::min(per_cu, kNarrowBlocksPerCU);
@@ -107,8 +109,7 @@ hipError_t launch_narrow_fused(const GemmParams& p, hipStream_t s, hipEvent_t ev
     const int64_t units = (int64_t)p.max_subs * nch;
     const int64_t grid = std::min<int64_t>(units, (int64_t)per_cu * cus);
     if (grid <= 0) return record_pair(ev0, ev1, s);
-    hipExtLaunchKernelGGL(narrow_fused_kernel, dim3((unsigned)grid), dim3(kNarrowThreads), 0, s, ev0, ev1,
-                          0, p);
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kNarrowThreads), 0, s, ev0, ev1, 0, p);
     return hipGetLastError();
 }
 

@@ -54,9 +54,18 @@ struct NarrowBuf {
 // activation scale times the block's weight scale.  GEMM1 then stores h = silu(g) * up * w in
 // float32 (p.hf32), to be quantised per 128 columns by the next launch (a
 // group spans four units of different workgroups).
-template <bool kG1, bool kCoh = false, bool kW8 = false>
+//
+// kST: FP4 codes in the staged layout (16-row groups, one KiB per group and K
+// step).  A unit is then half of a staged column block: GEMM1 unit nc (32 I
+// columns) is rows 8 (nc & 1) .. + 7 of groups 8 (nc >> 1) .. + 7, GEMM2 unit
+// nc (64 H columns) the same rows of its block's groups, and MFMA tile t takes
+// groups 2t and 2t + 1 (lanes l16 < 8 and >= 8), so every tile's loads are two
+// contiguous 512-byte runs per K step.  In GEMM1 a tile then holds gate (group
+// 2t) and up (group 2t + 1) of the I columns 32 nc + 4 j + t, j < 8.
+template <bool kG1, bool kCoh = false, bool kW8 = false, bool kST = false>
 MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
     static_assert(!(kCoh && kW8), "block-FP8 weights run as separate launches");
+    static_assert(!(kST && kW8), "the staged layout is one of packed FP4 codes");
     using Cfg = NarrowCfg<kG1, kW8>;
     constexpr int KC = Cfg::KC, NBUF = Cfg::NBUF;
     // partial accumulators, two buffers: unit j writes buffer j % 2, whose
@@ -91,8 +100,15 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
     const int kr = (nk + kNarrowWaves - 1) / kNarrowWaves;
     const int nchunk = (kr + KC - 1) / KC;
 
+    // staged layout: group and row of this lane's weight row in tile t of chunk nc
+    auto sgroup = [&](int nc, int t) { return 8 * (nc >> 1) + 2 * t + (l16 >> 3); };
+    const int srow_lo = l16 & 7;
     // weight row (= output column) of this lane in tile t of column chunk nc
     auto brow = [&](int nc, int t) -> int {
+        if constexpr (kST) {
+            const int g = sgroup(nc, t), c = 8 * (nc & 1) + srow_lo;
+            return kG1 ? staged_w13_row(g, c, p.I) : staged_w2_row(g, c);
+        }
         if (kG1) {
             const int icol = nc * Cfg::kCols + (t & 1) * 16 + l16;
             return w13_row(icol, t >> 1, p.I, p.w13_il);  // tiles 0, 1 gate; 2, 3 up
@@ -125,7 +141,9 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
 #pragma unroll
                 for (int t = 0; t < kNT; ++t) {
                     const int br = brow(nc, t);
-                    const uint8_t* row = wq_e + (int64_t)br * (K / kRow) + ks * (kKStep / kRow);
+                    const uint8_t* row =
+                        kST ? wq_e + ((int64_t)sgroup(nc, t) * nk + ks) * kStagedBlock + (8 * (nc & 1) + srow_lo) * 64
+                            : wq_e + (int64_t)br * (K / kRow) + ks * (kKStep / kRow);
                     bf.b[jj][t] = *reinterpret_cast<const v4i*>(row);
                     if constexpr (kW8) {
                         bf.b2[jj][t] = *reinterpret_cast<const v4i*>(row + 64);
@@ -236,14 +254,20 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
             __syncthreads();
             // lane holds rows 4 lg + i (i < 4), column l16 of a tile
             if (kG1) {
-                // wave 0: I columns [c, c+16) (tiles 0, 2); wave 1: [c+16, c+32) (tiles 1, 3)
+                // canonical: wave 0 takes I columns [c, c+16) (gate tile 0, up tile 2),
+                // wave 1 [c+16, c+32) (tiles 1, 3); staged: wave w takes tiles 2w and
+                // 2w + 1, lane l16 < 8 tile 2w, else 2w + 1, gate from the tile's
+                // lane j = l16 & 7 and up from its lane 8 + j
+                const int gt = kST ? 2 * wave + (l16 >> 3) : wave, ut = kST ? gt : 2 + wave;
+                const int gl = kST ? 16 * lg + srow_lo : lane, ul = kST ? gl + 8 : lane;
+                const int icol = kST ? 32 * nc + 4 * srow_lo + gt : nc * Cfg::kCols + wave * 16 + l16;
                 float h[4] = {0.f, 0.f, 0.f, 0.f};
                 if (wave < 2) {
-                    v4f g = s_red[0][wave][lane], u = s_red[0][2 + wave][lane];
+                    v4f g = s_red[0][gt][gl], u = s_red[0][ut][ul];
 #pragma unroll
                     for (int w = 1; w < kNarrowWaves; ++w) {
-                        g += s_red[w][wave][lane];
-                        u += s_red[w][2 + wave][lane];
+                        g += s_red[w][gt][gl];
+                        u += s_red[w][ut][ul];
                     }
                     const v4f wr = *reinterpret_cast<const v4f*>(&s_w[j][4 * lg]);
 #pragma unroll
@@ -260,7 +284,6 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
                 if constexpr (kW8) {
                     // h in float32; its 128-column groups are quantised by the next launch
                     if (wave < 2) {
-                        const int icol = nc * Cfg::kCols + wave * 16 + l16;
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
                             if (4 * lg + i < valid) p.hf32[(int64_t)(p0 + 4 * lg + i) * p.I + icol] = h[i];
@@ -270,7 +293,6 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
                 // an E4M3 group is the unit's 32 I columns: both waves' maxima
                 __syncthreads();
                 if (wave < 2) {
-                    const int icol = nc * Cfg::kCols + wave * 16 + l16;
                     const v4f m0 = *reinterpret_cast<const v4f*>(&s_amax[0][4 * lg]);
                     const v4f m1 = *reinterpret_cast<const v4f*>(&s_amax[1][4 * lg]);
 #pragma unroll

@@ -4,6 +4,7 @@
 // (16 bytes) per lane, so a wave reads 1 KiB of contiguous input per step.
 #include "common.h"
 #include "kernels.h"
+#include "mfma.h"
 
 namespace moe {
 
@@ -104,6 +105,44 @@ hipError_t launch_pack_weights(const uint16_t* w, int64_t rows, int cols, uint8_
 }  // namespace moe
 
 namespace moe {
+
+// Packed FP4 codes [mats][rows][cols/2] in canonical row order -> the staged
+// layout: thread i writes the 16-byte piece i of the output (matrix, group g,
+// K step ks, row c of the group, piece q of its 64 bytes) from row
+// staged_w*_row(g, c) of the same matrix.  Writes are contiguous, reads are
+// 16-byte pieces of rows.
+template <bool kW13>
+__global__ __launch_bounds__(kQuantThreads) void stage_weights_kernel(const uint8_t* __restrict__ w,
+                                                                      int64_t tasks, int rows, int cols,
+                                                                      uint8_t* __restrict__ out) {
+    const int nk = cols / 128;
+    const int64_t per_mat = (int64_t)rows * nk * 4;     // 16-byte pieces of one matrix
+    for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < tasks;
+         i += (int64_t)gridDim.x * kQuantThreads) {
+        const int64_t mat = i / per_mat;
+        const int64_t r = i - mat * per_mat;
+        const int q = (int)(r & 3), c = (int)((r >> 2) & 15);
+        const int64_t blk = r >> 6;                        // g * nk + ks
+        const int g = (int)(blk / nk), ks = (int)(blk - (int64_t)g * nk);
+        const int row = kW13 ? staged_w13_row(g, c, rows / 2) : staged_w2_row(g, c);
+        const uint8_t* src = w + (mat * rows + row) * (int64_t)(cols / 2) + ks * 64 + q * 16;
+        reinterpret_cast<uint4*>(out)[i] = *reinterpret_cast<const uint4*>(src);
+    }
+}
+
+hipError_t launch_stage_weights(const uint8_t* w, int64_t mats, int rows, int cols, bool w13, uint8_t* out,
+                                hipStream_t s) {
+    const int64_t tasks = mats * rows * (int64_t)(cols / 32);
+    if (tasks == 0) return hipSuccess;
+    if (w13)
+        hipLaunchKernelGGL(stage_weights_kernel<true>, dim3(grid_for(tasks)), dim3(kQuantThreads), 0, s, w,
+                           tasks, rows, cols, out);
+    else
+        hipLaunchKernelGGL(stage_weights_kernel<false>, dim3(grid_for(tasks)), dim3(kQuantThreads), 0, s, w,
+                           tasks, rows, cols, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_scales_kmajor(const uint8_t* sf, int64_t mats, int rows, int cols, uint8_t* out,
                                 hipStream_t s) {
     const int steps = cols / 128;

@@ -144,14 +144,26 @@ class DeviceLayer:
         self.w2sf_k = m.scales_kmajor(self.w2sf, w.I)
         self.d = m.dims(w.T, w.H, w.I, w.E, w.topk, w.score_fn, w.renorm)
         self.ws = m.new_workspace(self.d)
+        self._staged = None
 
-    def forward(self, use_logits=True, flags=0):
+    def staged(self):
+        """The weight codes in the staged layout (made on first use)."""
+        if self._staged is None:
+            m = lib()
+            self._staged = (m.stage_weights(self.w13q, True), m.stage_weights(self.w2q, False))
+        return self._staged
+
+    def forward(self, use_logits=True, flags=0, staged=False):
+        """One layer call; staged: with the staged weight codes (FLAG_W_STAGED)."""
         m = lib()
+        w13q, w2q = self.staged() if staged else (self.w13q, self.w2q)
+        if staged:
+            flags |= m.FLAG_W_STAGED
         if self.topk_idx is not None and not use_logits:
-            y = m.forward(self.d, self.x, self.w13q, self.w13sf_k, self.w2q, self.w2sf_k, self.ws,
+            y = m.forward(self.d, self.x, w13q, self.w13sf_k, w2q, self.w2sf_k, self.ws,
                           topk_idx=self.topk_idx, topk_w=self.topk_w, flags=flags)
         else:
-            y = m.forward(self.d, self.x, self.w13q, self.w13sf_k, self.w2q, self.w2sf_k, self.ws,
+            y = m.forward(self.d, self.x, w13q, self.w13sf_k, w2q, self.w2sf_k, self.ws,
                           logits=self.logits, flags=flags)
         torch.cuda.synchronize()
         status = int(m.intermediates(self.d, self.ws)["status"].item())

@@ -211,19 +211,27 @@ def _big(name, tokens=None):
 
 @pytest.mark.parametrize("name", ["dsv3_prefill", "dsv3_skewed"])
 def test_forward_full_size_every_token(name):
-    """The DeepSeek-V3-like shapes in full: every token's y and every pair's hq
-    (the whole 56-step K loop, every m-tile of every expert, the skewed workload's
-    hot and near-empty experts) against the oracle on all tokens."""
+    """The DeepSeek-V3-like shapes in full, with the staged weight codes the
+    benchmark runs: every token's y and every pair's hq (the whole 56-step K loop,
+    every m-tile of every expert, the skewed workload's hot and near-empty experts)
+    against the oracle on all tokens; then the canonical layout, bit for bit."""
     w = W.WORKLOADS[name]
     _log(f"forward {name} (every token)")
     dl, ref = _big(name)
-    y = dl.forward()
+    y = dl.forward(staged=True)
     inter = dl.intermediates()
     assert np.array_equal(inter["topk_idx"], ref["topk_idx"])
     G.check_bucketize(inter, ref["topk_idx"], w.E)
     assert np.array_equal(inter["xq"], ref["xq"])
     assert np.array_equal(inter["xsf"], ref["xsf"])
     _check_layer(inter, y, ref, w, name)
+    y_c = dl.forward()
+    assert np.array_equal(G.y_bits(y_c), G.y_bits(y)), "canonical and staged weight layouts differ"
+    # hq row by routed pair (the order of pairs inside an expert's segment is not fixed)
+    inter_c = dl.intermediates()
+    so, so_c = inter["slot_of"].reshape(-1), inter_c["slot_of"].reshape(-1)
+    assert np.array_equal(inter_c["hq"][so_c], inter["hq"][so])
+    assert np.array_equal(inter_c["hsf"][so_c], inter["hsf"][so])
 
 
 def _fused_waves(w):
@@ -273,7 +281,7 @@ def test_forward_full256_every_expert_tail(flags):
     dl = _BIG.get(("full256", "layer")) or G.DeviceLayer(w)
     _BIG[("full256", "layer")] = dl
     f = m.FLAG_ONE_LAUNCH if flags == "one-launch" else m.FLAG_NONE
-    y = dl.forward(flags=f)
+    y = dl.forward(flags=f, staged=True)
     inter = dl.intermediates()
     counts = inter["counts"]
     ragged = int(((counts % 128) != 0).sum())
@@ -286,6 +294,8 @@ def test_forward_full256_every_expert_tail(flags):
     assert np.array_equal(inter["topk_idx"], ref["topk_idx"])
     G.check_bucketize(inter, ref["topk_idx"], w.E)
     _check_layer(inter, y, ref, w, f"full256 {flags}", tokens=toks)
+    y_c = dl.forward(flags=f)
+    assert np.array_equal(G.y_bits(y_c), G.y_bits(y)), "canonical and staged weight layouts differ"
 
 
 # Shapes whose one-launch list has several expert waves on 256 CUs (3072 rows per
@@ -336,9 +346,10 @@ def test_workspace_poisoned_except_counters():
 @pytest.mark.parametrize("w", [RAGGED, W.WORKLOADS["decode"]], ids=lambda w: w.name)
 def test_weight_layout_flags(w):
     """Pre-interleaved W13 (the pages' gran-8 gate/up interleave, built by the
-    oracle's interleave from the oracle-packed weights) and per-row weight scales
-    give the oracle's result on every GEMM path, bit-identical to the canonical
-    layout."""
+    oracle's interleave from the oracle-packed weights), per-row weight scales and
+    the staged weight codes give the oracle's result on every GEMM path (the
+    ragged shape has partial last n-tiles in both GEMMs), bit-identical to the
+    canonical layout."""
     m = G.lib()
     _log(f"weight layout flags {w.name}")
     dl = G.DeviceLayer(w)
@@ -355,10 +366,13 @@ def test_weight_layout_flags(w):
         paths.append(("one kernel", m.FLAG_ONE_KERNEL))
     for name, flag in paths:
         base = G.y_bits(dl.forward(flags=flag))
+        s13, s2 = dl.staged()
         variants = {
             "interleaved": (iq_d, isf_k, dl.w2q, dl.w2sf_k, m.FLAG_W13_PREINTERLEAVED),
             "per-row scales": (dl.w13q, dl.w13sf, dl.w2q, dl.w2sf, m.FLAG_W_SCALES_PER_ROW),
             "both": (iq_d, isf_d, dl.w2q, dl.w2sf, m.FLAG_W13_PREINTERLEAVED | m.FLAG_W_SCALES_PER_ROW),
+            "staged": (s13, dl.w13sf_k, s2, dl.w2sf_k, m.FLAG_W_STAGED),
+            "staged, per-row scales": (s13, dl.w13sf, s2, dl.w2sf, m.FLAG_W_STAGED | m.FLAG_W_SCALES_PER_ROW),
         }
         for vname, (a13, b13, a2, b2, vf) in variants.items():
             y = m.forward(dl.d, dl.x, a13, b13, a2, b2, dl.ws, logits=dl.logits,
@@ -514,6 +528,8 @@ def test_tiled_gemms_many_tiles_per_workgroup(w):
         _log(f"  {name}")
         y = dl.forward(flags=flag)
         _check_layer(dl.intermediates(), y, ref, w, f"{w.name} {name}")
+        y_s = dl.forward(flags=flag, staged=True)
+        assert np.array_equal(G.y_bits(y_s), G.y_bits(y)), f"{name}: staged weight codes change y"
 
 
 def test_one_launch_reads_this_calls_h():
@@ -575,6 +591,34 @@ def test_one_kernel_layer_reads_this_calls_data():
         for dl, ref in zip((da, db, dc), refs):
             y = dl.forward(flags=m.FLAG_ONE_KERNEL)
             G.check_y(G.y_bits(y), ref["y"])
+
+
+def _staged_reference(q, is_w13):
+    """The staged layout written out from its definition: rows in groups of 16,
+    group g = 8 b + n holding canonical rows (n & 1) * I + 64 b + 4 c + n // 2
+    (W13) or 128 b + 8 c + n (W2), c < 16; per group, K step after K step, the
+    16 rows' 64 bytes of that step."""
+    mats, rows, kb = q.shape
+    nk = kb // 64
+    g = np.arange(rows // 16)[:, None]
+    c = np.arange(16)[None, :]
+    if is_w13:
+        row = (g & 1) * (rows // 2) + 64 * (g >> 3) + 4 * c + ((g & 7) >> 1)
+    else:
+        row = 128 * (g >> 3) + 8 * c + (g & 7)
+    assert np.array_equal(np.sort(row.reshape(-1)), np.arange(rows)), "not a permutation of the rows"
+    src = q.reshape(mats, rows, nk, 64)[:, row]               # [mats, groups, 16, nk, 64]
+    return np.ascontiguousarray(src.transpose(0, 1, 3, 2, 4)).reshape(mats, rows, kb)
+
+
+@pytest.mark.parametrize("mats,rows,cols,is_w13", [(3, 256, 256, True), (2, 768, 640, True),
+                                                   (4, 640, 384, False), (1, 7168, 2048, False),
+                                                   (2, 4096, 7168, True)])
+def test_stage_weights_layout(mats, rows, cols, is_w13):
+    m = G.lib()
+    q = np.random.default_rng(7).integers(0, 256, (mats, rows, cols // 2), dtype=np.uint8)
+    out = m.stage_weights(G.to_dev(q), is_w13).cpu().numpy()
+    assert np.array_equal(out, _staged_reference(q, is_w13))
 
 
 def test_scales_kmajor_is_a_transpose():

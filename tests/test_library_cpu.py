@@ -78,7 +78,10 @@ def test_forward_rejects_null_and_small_workspace_without_gpu():
                       # block-FP8 weights have their own scale layout and no gate/up interleave
                       m.FLAG_WEIGHTS_FP8_BLOCK128 | m.FLAG_W13_PREINTERLEAVED,
                       m.FLAG_WEIGHTS_FP8_BLOCK128 | m.FLAG_W_SCALES_PER_ROW,
-                      512, 1 << 31):                                           # unknown or conflicting
+                      m.FLAG_WEIGHTS_FP8_BLOCK128 | m.FLAG_W_STAGED,
+                      # the staged layout is made from the canonical gate-then-up row order
+                      m.FLAG_W_STAGED | m.FLAG_W13_PREINTERLEAVED,
+                      1024, 1 << 31):                                          # unknown or conflicting
         a.flags = bad_flags
         assert m._lib.moe_forward(ctypes.byref(a), None) == m.MOE_EINVAL
     # block-FP8 weights run on the narrow kernels in separate launches only
@@ -102,6 +105,19 @@ def test_quant_and_pack_reject_bad_sizes():
     assert m._lib.moe_quant_act(p, 4, 48, p, p, None) == m.MOE_EINVAL
     assert m._lib.moe_pack_weights(p, 4, 0, p, p, None) == m.MOE_EINVAL
     assert m._lib.moe_quant_act(p, 0, 64, p, p, None) == m.MOE_OK            # empty is a no-op
+
+
+def test_stage_weights_rejects_bad_sizes_without_gpu():
+    m = _lib()
+    p = ctypes.c_void_p(1 << 20)
+    q = ctypes.c_void_p(1 << 28)                                               # never dereferenced
+    assert m._lib.moe_stage_weights(p, 2, 192, 256, 1, q, None) == m.MOE_EINVAL    # rows % 128
+    assert m._lib.moe_stage_weights(p, 2, 256, 192, 0, q, None) == m.MOE_EINVAL    # cols % 128
+    assert m._lib.moe_stage_weights(p, 2, 256, 256, 1, ctypes.c_void_p((1 << 28) + 8), None) == m.MOE_EINVAL
+    # output overlapping the input (2 x 256 x 128 bytes from 1 MiB)
+    assert m._lib.moe_stage_weights(p, 2, 256, 256, 1, ctypes.c_void_p((1 << 20) + 65536 - 16),
+                                    None) == m.MOE_EINVAL
+    assert m._lib.moe_stage_weights(p, 0, 256, 256, 1, q, None) == m.MOE_OK        # empty is a no-op
 
 
 def test_error_strings():
