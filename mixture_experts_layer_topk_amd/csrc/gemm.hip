@@ -624,31 +624,6 @@ struct TileEngine {
     }
 };
 
-// One tile, loaded, computed and stored on its own (the one-launch kernel).
-template <int BM, int BN, int WM, int WN, bool kG1, bool kCoh, bool kIL, bool kST>
-MOE_DEV void gemm_tile(const GemmParams& p, int mt, int ntile, uint8_t* smem) {
-    TileEngine<BM, BN, WM, WN, kG1, kCoh, kIL, kST> eng(p, smem);
-    const int4 rec = p.mtile_rec[mt];        // {expert, first position, rows}
-    eng.load_rows_now(rec, 0);
-    eng.set_tile(rec, ntile, 0);
-    eng.set_rows(rec.z);
-    eng.zero_acc();
-    eng.prologue(0);
-    int st = 0;                                 // stage of step ks
-    for (int ks = 0; ks < eng.nk; ++ks) {
-        const int st2 = eng.next_stage(eng.next_stage(st));
-        eng.step(eng.stage_ptr(st), ks == 0, [] {}, [&] {
-            if (ks + 2 >= eng.nk) return false;
-            eng.issue(st2);
-            return true;
-        });
-        st = eng.next_stage(st);
-    }
-    eng.finish();
-    eng.epilogue(rec, ntile, 0);
-    __syncthreads();
-}
-
 // n-tiles of GEMM1 (BN/2 columns of I, gate and up) or GEMM2 (BN columns of
 // H); the last one may be partial (I and H are multiples of 128).
 template <int BN>
@@ -727,54 +702,143 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
     }
 }
 
+// Waits until ready[mt] counts every GEMM1 n-tile of m-tile mt.  Every lane
+// polls and the loop branches on the first lane's value, so the wait is uniform
+// (no divergent loop inside the K pipeline).  Bounded: past the spin limit
+// thread 0 sets *p.status and the wait gives up, so the output is wrong but the
+// kernel ends.  The bounds are read from p here rather than kept live in the
+// caller's K loop.
+template <int BN>
+MOE_DEV void wait_ready(const GemmParams& p, int mt) {
+    const int need = gemm_ntiles<BN>(p, true);
+    const int spin_limit = p.spin_limit > 0 ? p.spin_limit : kSpinLimit;
+    for (int n = 0;;) {
+        const int v = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(p.ready + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (v >= need) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++n >= spin_limit) {
+            if (threadIdx.x == 0) __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+    }
+}
+
+// A run of one workgroup's consecutive list entries of one family (entries
+// tile, tile + grid, ... while they are GEMM1 tiles, or GEMM2 tiles), with the
+// two-launch kernel's cross-tile pipeline: the next entry's rows are fetched
+// and its first two K steps loaded during the current entry's K loop.  Returns
+// the first entry after the run (of the other family, or past the list).
+//   GEMM1: h is stored device-coherent; after a tile's epilogue every thread
+//          waits for its stores (vmcnt(0)), and after a barrier thread 0 adds
+//          one to ready[m-tile].
+//   GEMM2: the first tile of the run waits for ready[m] before any load; a
+//          pipelined next tile's wait runs at the start of the current tile's
+//          K loop, before its loads (at the last two K steps) are issued.
+// A GEMM2 entry waits only for GEMM1 entries earlier in the list, GEMM1
+// entries never wait, and every workgroup is resident: the waits end.
+// List entry -> (family, m-tile, n-tile), seeking from the first segment (a
+// few scalar steps per tile, so no cursor stays live across the K loop).
+// Returns false past the end of the list.
+template <int BN>
+MOE_DEV bool fused_entry(const GemmParams& p, int entry, int* g1, int* mt, int* ntile) {
+    const int NT1 = gemm_ntiles<BN>(p, true), NT2 = gemm_ntiles<BN>(p, false);
+    if (entry >= p.mtile_off[p.E] * (NT1 + NT2)) return false;
+    const int nw = (p.E + p.wave_experts - 1) / p.wave_experts;
+    sched::FusedCursor cur;
+    cur.seek(entry, nw, p.wave_experts, p.E, p.mtile_off, NT1, NT2);
+    cur.tile(entry, NT1, NT2, mt, ntile);
+    *g1 = cur.sg.g1;
+    return true;
+}
+
+template <int BM, int BN, int WM, int WN, bool kG1, bool kIL, bool kST>
+MOE_DEV int fused_run(const GemmParams& p, int tile, int mt, int ntile, uint8_t* smem) {
+    using Eng = TileEngine<BM, BN, WM, WN, kG1, true, kG1 && kIL, kST>;
+    Eng eng(p, smem);
+    const int nk = eng.nk;
+    const bool chain = nk >= (kG1 ? 5 : 2);
+    if (!kG1) wait_ready<BN>(p, mt);
+    int4 rec = p.mtile_rec[mt];                  // {expert, first position, rows}
+    int buf = 0, st = 0;
+    eng.load_rows_now(rec, buf);                 // (its barrier also ends the wait above)
+    eng.set_tile(rec, ntile, buf);
+    eng.prologue(st);
+    for (;;) {
+        const int nxt = tile + gridDim.x;
+        int g1_n = kG1, mt_n = mt, nt_n = ntile;
+        const bool has_next = fused_entry<BN>(p, nxt, &g1_n, &mt_n, &nt_n) && (g1_n != 0) == kG1;
+        if (!has_next) mt_n = mt, nt_n = ntile;
+        const int4 rec_n = p.mtile_rec[mt_n];
+        const bool pf = has_next && chain;
+        if (!kG1 && pf) wait_ready<BN>(p, mt_n);
+        eng.set_rows(rec.z);
+        eng.zero_acc();
+        for (int ks = 0; ks < nk; ++ks) {
+            const int st2 = Eng::next_stage(Eng::next_stage(st));
+            eng.step(
+                eng.stage_ptr(st), ks == 0,
+                [&] {
+                    if (pf) {
+                        if (ks == 1 || ks == 2) eng.fetch_rows(rec_n, buf ^ 1, ks - 1);
+                        if (ks == nk - 2) eng.set_tile(rec_n, nt_n, buf ^ 1);
+                    }
+                },
+                [&] {
+                    if (ks + 2 >= nk && !pf) return false;
+                    eng.issue(st2);
+                    return true;
+                });
+            st = Eng::next_stage(st);
+        }
+        eng.finish();
+        eng.epilogue(rec, ntile, buf);
+        if (kG1) {
+            // every thread's coherent h stores have completed (vmcnt(0)) before the barrier
+            __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8) | (0 << 14));
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_fetch_add(p.ready + mt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (!has_next) {
+            __syncthreads();                     // LDS free for the next run's engine
+            return nxt;
+        }
+        tile = nxt;
+        mt = mt_n;
+        ntile = nt_n;
+        rec = rec_n;
+        buf ^= 1;
+        if (!pf) {        // K too short to hide the next tile's set-up: do it here
+            if (!kG1) wait_ready<BN>(p, mt);
+            eng.load_rows_now(rec, buf);
+            eng.set_tile(rec, ntile, buf);
+            eng.prologue(st);
+        }
+    }
+}
+
 // GEMM1 -> SwiGLU -> GEMM2 in one persistent launch ("MegaMoE" notes,
 // "Scheduler" and "Wave"; "MegaMoE：把通信和计算融合到一个 Mega Kernel", wave-based
 // expert processing).  Experts are cut into waves of p.wave_experts; the tile
 // list is GEMM1(wave 0), GEMM1(wave 1), GEMM2(wave 0), GEMM1(wave 2),
 // GEMM2(wave 1), ..., GEMM2(last wave), each run in the grouped order, and
-// workgroup slot q takes list entries q, q + grid, ... .  A GEMM1 tile adds one
-// to ready[m] once its h columns are stored; a GEMM2 tile of m-tile m starts
-// when ready[m] counts every GEMM1 n-tile of m (the bucketing stage of the call
-// zeroes ready[] before this launch).  A GEMM2 entry only waits for GEMM1
-// entries earlier in the list and every workgroup is resident (one per CU),
-// so the waits always end; a wait longer than kSpinLimit polls stops, sets
-// *p.status and lets the tile run (its output is then wrong, never a hang).
+// workgroup slot q takes list entries q, q + grid, ...  Consecutive entries of
+// one family run as one pipelined run (fused_run).  A GEMM1 tile adds one to
+// ready[m] once its h columns are stored; a GEMM2 tile of m-tile m starts
+// loading when ready[m] counts every GEMM1 n-tile of m (the bucketing stage of
+// the call zeroes ready[] before this launch).  A wait longer than kSpinLimit
+// polls stops, sets *p.status and lets the tile run (its output is then wrong,
+// never a hang).
 template <int BM, int BN, int WM, int WN, bool kIL, bool kST>
 __global__ __launch_bounds__(64 * WM * WN, 1) void fused_gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    const int tid = threadIdx.x;
-    const int NT1 = gemm_ntiles<BN>(p, true), NT2 = gemm_ntiles<BN>(p, false);
-    const int ew = p.wave_experts;
-    const int nw = (p.E + ew - 1) / ew;
-    const int spin_limit = p.spin_limit > 0 ? p.spin_limit : kSpinLimit;
-    sched::FusedCursor cur;
-    const int total = p.mtile_off[p.E] * (NT1 + NT2);
-    for (int tile = xcd_slot(); tile < total; tile += gridDim.x) {
-        cur.seek(tile, nw, ew, p.E, p.mtile_off, NT1, NT2);
-        int mt, ntile;
-        cur.tile(tile, NT1, NT2, &mt, &ntile);
-        if (cur.sg.g1) {
-            gemm_tile<BM, BN, WM, WN, true, true, kIL, kST>(p, mt, ntile, smem);
-            // every thread's coherent h stores have completed (vmcnt(0)) before the barrier
-            __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8) | (0 << 14));
-            __syncthreads();
-            if (tid == 0)
-                __hip_atomic_fetch_add(p.ready + mt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            if (tid == 0) {
-                int n = 0;
-                while (__hip_atomic_load(p.ready + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                       NT1) {
-                    __builtin_amdgcn_s_sleep(1);
-                    if (++n >= spin_limit) {
-                        __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                }
-            }
-            __syncthreads();
-            gemm_tile<BM, BN, WM, WN, false, true, false, kST>(p, mt, ntile, smem);
-        }
+    int tile = xcd_slot(), g1, mt, ntile;
+    while (fused_entry<BN>(p, tile, &g1, &mt, &ntile)) {
+        if (g1)
+            tile = fused_run<BM, BN, WM, WN, true, kIL, kST>(p, tile, mt, ntile, smem);
+        else
+            tile = fused_run<BM, BN, WM, WN, false, kIL, kST>(p, tile, mt, ntile, smem);
     }
 }
 
