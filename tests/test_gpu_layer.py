@@ -448,6 +448,46 @@ def test_forward_external_topk_with_masked_slots():
     G.check_y(G.y_bits(y), ref["y"])
 
 
+def _combine_of(o_bits, slot_of, H):
+    """y from the GPU's own GEMM2 rows, by the combine's definition: float32 sums
+    in slot order (0 + row of slot 0 + row of slot 1 ...), skipped slots adding
+    nothing, rounded to BF16."""
+    acc = np.zeros((slot_of.shape[0], H), np.float32)
+    for j in range(slot_of.shape[1]):
+        pos = slot_of[:, j]
+        ok = pos >= 0
+        acc[ok] = acc[ok] + C.bf16_value(o_bits[pos[ok]])
+    return C.bf16_bits(acc)
+
+
+# The narrow path with a caller's top-k: routing through the one-workgroup
+# bucketing (decode, 8 tokens) and the multi-workgroup one (40 tokens)
+COMBINE_SHAPES = [W.WORKLOADS["decode"], W.Workload("narrow40", T=40, H=512, I=256, E=64, topk=4)]
+
+
+@pytest.mark.parametrize("w", COMBINE_SHAPES, ids=lambda w: w.name)
+def test_narrow_path_combine_is_exact(w):
+    """On the narrow GEMMs, y equals the slot-order combine of the GPU's own GEMM2
+    rows bit for bit, with masked slots and one token with none (y = 0), and
+    matches the oracle."""
+    _log(f"narrow path combine {w.name}")
+    idx, wt = W.gen_external_topk(w, mask_frac=0.25)
+    idx[0] = -1                                  # token 0: no expert at all
+    dl = G.DeviceLayer(w, external_topk=(idx, wt))
+    assert w.T * w.topk <= 3 * w.E, "the shape must take the narrow GEMMs"
+    y = dl.forward(use_logits=False)
+    inter = dl.intermediates()
+    o = inter["o"].view(np.uint16)
+    yb = G.y_bits(y)
+    assert np.array_equal(yb, _combine_of(o, inter["slot_of"], w.H)), "y is not the combine of GEMM2's rows"
+    assert not yb[0].any(), "a token without experts must give y = 0"
+    ref = _oracle_full(w, (idx, wt))
+    G.check_y(yb, ref["y"], label=f"{w.name} y")
+    # a second call on the same workspace (the counters start from zero again)
+    y2 = dl.forward(use_logits=False)
+    assert np.array_equal(G.y_bits(y2), yb)
+
+
 def test_forward_all_tokens_one_expert():
     w = W.Workload("hot", T=700, H=256, I=128, E=8, topk=1)
     _log("forward one hot expert")
