@@ -36,7 +36,7 @@ PEAK_MFMA_FP8_TFLOPS = 5000.0      # MI355X dense FP8-rate MFMA (FP8 x FP4 issue
 PEAK_HBM_GBS = 8000.0
 # workloads whose GEMMs stream more weight bytes than they have FLOPs to hide
 HBM_BOUND = {"decode"}
-KERNEL_SOURCES = ("gemm.hip", "narrow.hip", "narrow_dev.h", "mfma.h", "common.h", "kernels.h")
+KERNEL_SOURCES = ("gemm.hip", "narrow.hip", "narrow_dev.h", "mfma.h", "common.h", "kernels.h", "sched.h")
 NARROW_ROWS_PER_EXPERT = 3         # moe_forward's choice between the two GEMM kernel families
 
 
