@@ -479,6 +479,7 @@ int moe_forward(const moe_args_t* a, hipStream_t s) {
         lp.y = a->y;
         lp.count = at<unsigned>(ws, c.arrive) + 4;
         lp.exits = at<unsigned>(ws, c.arrive) + 8;
+        lp.count2 = at<unsigned>(ws, c.arrive) + 12;
         lp.status = sp.status;
         err = moe::launch_layer_small(rp, sp, gp, lp, s);
         for (int i = 1; i < MOE_NUM_STAGE_EVENTS && err == hipSuccess && ev; ++i)

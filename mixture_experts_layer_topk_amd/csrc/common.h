@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -66,6 +68,29 @@ MOE_DEV int e2m1_block_exp(float amax) { return block_exp<0x400000u, 2>(amax); }
 
 // 2^-e as a float for e in [-127, 127] (2^-127 is a float32 subnormal).
 MOE_DEV float exp2_neg(int e) { return __builtin_ldexpf(1.0f, -e); }
+
+// *p = v, device-coherent when kCoh (a write-through store that other XCDs'
+// loads see once it has completed; 16-byte values as four dword stores), for
+// data handed to other workgroups inside the same launch.
+template <bool kCoh, class T>
+MOE_DEV void put(T* p, T v) {
+    if constexpr (!kCoh) {
+        *p = v;
+    } else if constexpr (sizeof(T) == 16) {
+        const uint4 u = __builtin_bit_cast(uint4, v);
+        uint32_t* q = reinterpret_cast<uint32_t*>(p);
+        __hip_atomic_store(q + 0, u.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(q + 1, u.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(q + 2, u.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(q + 3, u.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        static_assert(sizeof(T) == 1 || sizeof(T) == 2 || sizeof(T) == 4 || sizeof(T) == 8, "store size");
+        using U = std::conditional_t<sizeof(T) == 1, uint8_t,
+                  std::conditional_t<sizeof(T) == 2, uint16_t, std::conditional_t<sizeof(T) == 4, uint32_t, uint64_t>>>;
+        __hip_atomic_store(reinterpret_cast<U*>(p), __builtin_bit_cast(U, v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
 
 // Two float32 values to E4M3 codes in the low 16 bits (first value in the low
 // byte), nearest even, by the gfx950 conversion instruction.  Inputs must be

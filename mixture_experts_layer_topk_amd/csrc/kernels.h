@@ -184,13 +184,14 @@ hipError_t launch_combine(const uint16_t* o, const int32_t* slot_of, int64_t T, 
                           uint16_t* y, hipStream_t s);
 
 // The whole layer in one cooperative launch for T * topk <= 1024 (routing and
-// bucketing in one workgroup, narrow GEMMs, combine), phases separated by
-// grid barriers on two counters that are zero between launches.
+// bucketing in one workgroup, narrow GEMMs, combine), phases handed over by
+// arrival counts that are zero between launches.
 struct LayerParams {
     uint16_t* y;                // [T, H] layer output
-    unsigned* count;            // barrier arrivals (zero on entry, reset on exit)
+    unsigned* count;            // workgroups done with the routing phase (zero on entry, reset on exit)
+    unsigned* count2;           // workgroups done with GEMM2 (zero on entry, reset on exit)
     unsigned* exits;            // workgroups that have left (zero on entry, reset on exit)
-    int* status;                // [1] set to 2 if a barrier wait gave up
+    int* status;                // [1] set to 2 if a hand-off wait gave up
     int npl;                    // logits per lane of the routing waves (set by the launcher)
 };
 bool layer_small_fits(int64_t T, int topk);

@@ -28,6 +28,22 @@ struct NarrowCfg {
     static constexpr int NBUF = kW8 ? 3 : (kG1 ? 2 : 4);
 };
 
+// LDS of the narrow GEMMs.  One block for every instance of narrow_gemm in a
+// kernel: GEMM1 and GEMM2 running one after the other in one launch share it
+// (static shared arrays inside the template would be allocated per instance,
+// doubling the LDS of such a kernel and halving its occupancy).
+struct NarrowLds {
+    v4f red2[2][kNarrowWaves][kNT][64];                 // partial accumulators, two buffers
+    int hdr[kBatch][4];                                 // expert, first position, rows, chunk
+    int arow[kBatch][kSubRows];                         // activation row of each unit row
+    __attribute__((aligned(16))) float w[kBatch][kSubRows];    // routing weight (GEMM1)
+    __attribute__((aligned(16))) float amax[2][16];
+};
+__device__ __forceinline__ NarrowLds& narrow_lds() {
+    __shared__ NarrowLds s;
+    return s;
+}
+
 template <int KC, bool kW8>
 struct NarrowBuf {
     v4i b[KC][kNT];             // FP4: the lane's 16 bytes; FP8: its first 16 of 32
@@ -46,6 +62,8 @@ struct NarrowBuf {
 // complete and then adds each finished unit to ready[sub-tile]; a GEMM2 batch
 // issues its first weight loads, waits until ready[] counts every GEMM1 unit
 // of each of its sub-tiles and then reads h with device-coherent loads.
+// GEMM2 stores o device-coherently too (the one-kernel layer's combine reads
+// it in the same launch).
 //
 // kW8: block-FP8 weights (E4M3 codes [E, N, K], one float32 scale per 128 x 128
 // block) and activations with one float32 scale per row per 128 K ("MonoMoe
@@ -70,11 +88,12 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
     constexpr int KC = Cfg::KC, NBUF = Cfg::NBUF;
     // partial accumulators, two buffers: unit j writes buffer j % 2, whose
     // previous readers (unit j - 2) finished before unit j - 1's barrier
-    __shared__ v4f s_red2[2][kNarrowWaves][kNT][64];
-    __shared__ int s_hdr[kBatch][4];                   // expert, first position, rows, chunk
-    __shared__ int s_arow[kBatch][kSubRows];           // activation row of each unit row
-    __shared__ __attribute__((aligned(16))) float s_w[kBatch][kSubRows];   // routing weight (GEMM1)
-    __shared__ __attribute__((aligned(16))) float s_amax[2][16];
+    NarrowLds& lds = narrow_lds();
+    v4f (&s_red2)[2][kNarrowWaves][kNT][64] = lds.red2;
+    int (&s_hdr)[kBatch][4] = lds.hdr;
+    int (&s_arow)[kBatch][kSubRows] = lds.arow;
+    float (&s_w)[kBatch][kSubRows] = lds.w;
+    float (&s_amax)[2][16] = lds.amax;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -326,7 +345,7 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 4 * lg + i;
-                    if (r < valid) p.o[(int64_t)(p0 + r) * p.H + col] = (uint16_t)f32_to_bf16(o[i]);
+                    if (r < valid) put<kCoh>(p.o + (int64_t)(p0 + r) * p.H + col, (uint16_t)f32_to_bf16(o[i]));
                 }
             }
         };
@@ -389,6 +408,7 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
             if (hr == 0 && hu < nunits)
                 __hip_atomic_fetch_add(p.ready + hu / nch, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+
     }
 }
 

@@ -127,7 +127,7 @@ MOE_DEV void route_token(const float (&v)[NPL], int E, int k, int score_fn, int 
 
 // Quantise x rows [T, H]: task i covers 8 elements of the flattened array;
 // workgroups of kThreads threads.
-template <int kThreads>
+template <int kThreads, bool kCoh = false>
 MOE_DEV void quant_rows(const RouteParams& p, int block, int nblocks) {
     const int64_t tasks = p.T * (p.H / 8);
     const int64_t stride = (int64_t)nblocks * kThreads;
@@ -158,12 +158,12 @@ MOE_DEV void quant_rows(const RouteParams& p, int block, int nblocks) {
                 float inv = exp2_neg(e);
                 uint32_t lo = e4m3_pack4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
                 uint32_t hi = e4m3_pack4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
-                *reinterpret_cast<uint2*>(p.xq + i * 8) = make_uint2(lo, hi);
+                put<kCoh>(reinterpret_cast<uint64_t*>(p.xq + i * 8), (uint64_t)lo | (uint64_t)hi << 32);
                 if ((i & 3) == 0) {
                     // scales K-step major: xsf[g / 4][t][g % 4] for group g of token t
                     const int64_t G = i >> 2, gpr = p.H / kGroup;
                     const int64_t t = G / gpr, g = G - t * gpr;
-                    p.xsf[(g >> 2) * (p.T * 4) + t * 4 + (g & 3)] = (uint8_t)(e + 127);
+                    put<kCoh>(p.xsf + (g >> 2) * (p.T * 4) + t * 4 + (g & 3), (uint8_t)(e + 127));
                 }
             }
         }
@@ -342,8 +342,9 @@ MOE_DEV void write_tables(const ScatterParams& p, const int* cnt, const int* off
 // expert contributes its pairs, m-tiles and sub-tiles as three 21-bit fields
 // of one 64-bit value (none of the sums reaches 2^21 at this size), and the
 // thread that owns an expert writes that expert's records itself.  Workgroups
-// of kThreads threads.
-template <int kThreads>
+// of kThreads threads.  kCoh: every table is stored device-coherently, for
+// workgroups of the same launch that read it after a hand-off.
+template <int kThreads, bool kCoh = false>
 MOE_DEV void bucket_small(const RouteParams& rp, const ScatterParams& sp, int npl) {
     using Scan = rocprim::block_scan<uint64_t, kThreads>;
     constexpr int kPer = kMaxExperts / kThreads;          // experts per thread
@@ -384,37 +385,37 @@ MOE_DEV void bucket_small(const RouteParams& rp, const ScatterParams& sp, int np
         const int o = (int)(x[j] & kField);
         int m = (int)((x[j] >> 21) & kField), u = (int)(x[j] >> 42);
         off[e] = o;
-        sp.counts_out[e] = c[j];
-        sp.offsets_out[e] = o;
-        sp.mtile_off[e] = m;
+        put<kCoh>(sp.counts_out + e, c[j]);
+        put<kCoh>(sp.offsets_out + e, o);
+        put<kCoh>(sp.mtile_off + e, m);
         for (int r = 0; r < c[j]; r += bm, ++m) {
-            sp.mtile_rec[m] = make_int4(e, o + r, min(bm, c[j] - r), 0);
-            sp.mtile_e[m] = e;
+            put<kCoh>(sp.mtile_rec + m, make_int4(e, o + r, min(bm, c[j] - r), 0));
+            put<kCoh>(sp.mtile_e + m, e);
         }
         for (int r = 0; r < c[j]; r += kSubRows, ++u)
-            sp.sub_rec[u] = make_int4(e, o + r, min(kSubRows, c[j] - r), 0);
+            put<kCoh>(sp.sub_rec + u, make_int4(e, o + r, min(kSubRows, c[j] - r), 0));
     }
     if (tid == 0) {
-        sp.offsets_out[E] = (int)(total & kField);
-        sp.mtile_off[E] = n_mtiles;
-        *sp.nsub = n_subs;
-        *sp.status = 0;
+        put<kCoh>(sp.offsets_out + E, (int)(total & kField));
+        put<kCoh>(sp.mtile_off + E, n_mtiles);
+        put<kCoh>(sp.nsub, n_subs);
+        put<kCoh>(sp.status, 0);
     }
     // records past the last tile are zero; the one-launch GEMMs' counters start at zero
     const int4 zero = make_int4(0, 0, 0, 0);
-    for (int m = n_mtiles + tid; m < sp.max_mtiles; m += kThreads) sp.mtile_rec[m] = zero;
-    for (int m = n_subs + tid; m < sp.max_subs; m += kThreads) sp.sub_rec[m] = zero;
-    for (int m = tid; m < sp.nready; m += kThreads) sp.ready[m] = 0;
+    for (int m = n_mtiles + tid; m < sp.max_mtiles; m += kThreads) put<kCoh>(sp.mtile_rec + m, zero);
+    for (int m = n_subs + tid; m < sp.max_subs; m += kThreads) put<kCoh>(sp.sub_rec + m, zero);
+    for (int m = tid; m < sp.nready; m += kThreads) put<kCoh>(sp.ready + m, 0);
     lds_barrier();                                        // off[] complete
     for (int i = tid; i < npairs; i += kThreads) {
         const int e = pair_exp[i];
         if (pair_rank[i] >= 0) {
             const int pos = off[e] + pair_rank[i];
-            sp.slot_src[pos] = i;
-            sp.slot_of[i] = pos;
-            sp.slot_w[pos] = pair_w[i];
+            put<kCoh>(sp.slot_src + pos, i);
+            put<kCoh>(sp.slot_of + i, pos);
+            put<kCoh>(sp.slot_w + pos, pair_w[i]);
         } else {
-            sp.slot_of[i] = -1;
+            put<kCoh>(sp.slot_of + i, -1);
         }
     }
 }
