@@ -408,7 +408,6 @@ MOE_DEV void narrow_gemm(const GemmParams& p, int bid, int G) {
             if (hr == 0 && hu < nunits)
                 __hip_atomic_fetch_add(p.ready + hu / nch, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-
     }
 }
 
