@@ -96,17 +96,18 @@ struct Cfg {
     static constexpr int kLds = kStages * kStage + kRowBytes;
     static constexpr int kAI = kABytes / 1024 / kWaves;   // 1 KiB load instructions per wave
     static constexpr int kBI = kBBytes / 1024 / kWaves;
-    // Scale tiles: one dword per lane, 64 rows per load, issued by the late
-    // waves only (wm = 1, waves kEarly .. 2 kEarly - 1): the early wave of a
-    // SIMD has the longer chain of work in a step (it waits on the barrier
-    // less), so the extra load instructions go to the late one (measured 1%
-    // faster).  Late wave kEarly + e loads B-scale blocks kSBE e ..
-    // kSBE e + kSBE - 1 and, if e < kSABlocks, A-scale block e.
+    // Scale tiles: one dword per lane, 64 rows per load.  Early wave e loads
+    // B-scale blocks kSBE e .. kSBE e + kSBE - 1, late wave kEarly + e the
+    // A-scale block e if e < kSABlocks.  The late wave's chain sets the end of
+    // a K step (its MFMAs, then its loads, fragment reads and the wait for its
+    // previous loads), while the early wave has time to spare before the
+    // matrix core is free for its MFMAs, so the B scales go to the early
+    // waves (GEMM1 -1.1% at the 256-expert shape, no change at 32 experts).
     static constexpr int kEarly = WN;
     static constexpr int kSABlocks = BM / 64, kSBBlocks = BN / 64;
     static constexpr int kSBE = kSBBlocks / kEarly;
-    static constexpr int kLoadsEarly = kAI + kBI;           // per wave per stage
-    static constexpr int kLoadsLate = kAI + kBI + kSBE;     // + 1 with an A-scale block
+    static constexpr int kLoadsEarly = kAI + kBI + kSBE;    // per wave per stage
+    static constexpr int kLoadsLate = kAI + kBI;            // + 1 with an A-scale block
     static_assert(kABytes % (1024 * kWaves) == 0 && kBBytes % (1024 * kWaves) == 0, "tile / waves");
     static_assert(BM % 64 == 0 && BN % 64 == 0, "scale tiles in whole 64-row loads");
     static_assert(MT >= 1 && NT >= 2 && NT % 2 == 0, "wave tile");
@@ -370,7 +371,8 @@ struct TileEngine {
                 b_src[j] = b_row(n) * (uint32_t)b_stride + c * 16;
             }
         }
-        // scale blocks of a late wave (an early wave's values are not used)
+        // scale blocks: B of an early wave, A of a late wave (the other values
+        // are not used)
         const int ew = L.wave % C::kEarly;
         sa_src = row_src(scale_slot_row(64 * (ew % C::kSABlocks) + L.lane)) * 4u;
         // B scales are staged in the B tile's LDS row order, regrouped by
@@ -401,12 +403,14 @@ struct TileEngine {
 #pragma unroll
         for (int j = 0; j < C::kBI; ++j)
             load_lds16<0>(ld_w + b_src[j], sB + (j * C::kWaves + wave) * 1024);
-        if (late) {
+        {
             const int ew = wave % C::kEarly;
             if (sa_wave) load_lds4<kAuxA>(ld_sa + sa_src, sSA + ew * 256);
+            if (!late) {
 #pragma unroll
-            for (int j = 0; j < C::kSBE; ++j)
-                load_lds4<0>(ld_sw + sb_src[j], sSB + (C::kSBE * ew + j) * 256);
+                for (int j = 0; j < C::kSBE; ++j)
+                    load_lds4<0>(ld_sw + sb_src[j], sSB + (C::kSBE * ew + j) * 256);
+            }
         }
         ld_a += BK;
         ld_w += kST ? kStagedBlock : BK / 2;
@@ -492,14 +496,18 @@ struct TileEngine {
 
     // One K step on stage `cur`.  The two waves of a SIMD (wm = 0 and wm = 1)
     // are de-phased: after the barrier that publishes the stage the early wave
-    // reads its fragments and then runs its MFMAs, the late wave first runs the
-    // MFMAs of the previous step (fragments already in registers) and then
-    // reads the stage, so one wave's LDS reads overlap the other's MFMAs.  The
-    // late wave runs its MFMAs at raised priority: when the early wave gets to
-    // its own MFMAs first, the late wave's still win the SIMD, so it can go on
-    // to its reads and loads while the early wave computes (without this the
-    // two waves' MFMAs interleave and the late wave's reads and loads end up
-    // after every MFMA of the step, with the matrix core idle).
+    // issues its loads, reads its fragments and then runs its MFMAs; the late
+    // wave first runs the MFMAs of the previous step (fragments already in
+    // registers), then issues its loads and reads the stage, so one wave's
+    // loads and LDS reads overlap the other's MFMAs.  Loads go before the
+    // fragment reads: the late wave's wait for its previous loads ends its
+    // chain, and the fragments it reads are needed only at the next step
+    // (GEMM1 -1.5 to -2.4%).  The late wave runs its MFMAs at raised priority:
+    // when the early wave gets to its own MFMAs first, the late wave's still
+    // win the SIMD, so it can go on to its loads and reads while the early
+    // wave computes (without this the two waves' MFMAs interleave and the
+    // late wave's loads and reads end up after every MFMA of the step, with
+    // the matrix core idle).
     // `loads()` issues this step's loads (step + 2, or one of the next tile's
     // first two) and returns whether it issued any; `extra()` issues whatever
     // must be retired by this step's wait.  The wait retires everything but
@@ -511,10 +519,10 @@ struct TileEngine {
             mfmas();
             __builtin_amdgcn_s_setprio(0);
         }
-        read_frags(cur);
-        __builtin_amdgcn_sched_barrier(0);
         extra();
         const bool issued = loads();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(cur);
         __builtin_amdgcn_sched_barrier(0);
         if (!late) mfmas();
         if (issued)
