@@ -86,11 +86,11 @@ typedef struct moe_dims {
  * two launches at the DeepSeek-V3-like and 256-expert shapes, so it is not
  * the default.  MOE_FLAG_ONE_KERNEL runs the whole layer (routing, bucketing,
  * quantisation, the narrow GEMMs and the combine) as one cooperative launch
- * whose phases are separated by grid barriers ("MonoMoe kernel — design" §1);
- * it needs T * topk <= 1024 (else MOE_EUNSUPPORTED) and implies the narrow
- * GEMMs.  On one MI355X its grid barriers (cache write-backs between XCDs)
- * cost more than the launch boundaries they replace, so it is not the
- * default either.  MOE_FLAG_NARROW | MOE_FLAG_ONE_LAUNCH runs the narrow GEMM1
+ * whose phases hand over by arrival counts ("MonoMoe kernel — design" §1;
+ * "MegaMoE：把通信和计算融合到一个 Mega Kernel", arrival-count polling); it
+ * needs T * topk <= 1024 (else MOE_EUNSUPPORTED) and implies the narrow GEMMs.
+ * On one MI355X its waits cost more than the launch boundaries they replace
+ * (84 against 44 us at the decode shape), so it is not the default either.  MOE_FLAG_NARROW | MOE_FLAG_ONE_LAUNCH runs the narrow GEMM1
  * -> SwiGLU -> GEMM2 as one launch whose GEMM2 units wait on per-sub-tile
  * ready counters; measured slower than the two narrow launches at the decode
  * shape (GEMM2 cannot start before the slowest GEMM1 unit of its rows), so it
@@ -124,9 +124,10 @@ typedef struct moe_dims {
  *                       of polling; a wait that gives up sets the status word
  *                       (moe_check_status reports MOE_ETIMEOUT) and the output
  *                       is then invalid.  For exercising the failure report;
- *                       MOE_EINVAL together with ONE_KERNEL, whose grid
- *                       barriers guard the routing tables the later phases
- *                       index with. */
+ *                       MOE_EINVAL together with ONE_KERNEL, whose routing
+ *                       hand-off guards the tables the later phases index
+ *                       with (giving up there early could read stale
+ *                       indices). */
 #define MOE_FLAG_W13_PREINTERLEAVED 16u
 #define MOE_FLAG_W_SCALES_PER_ROW 32u
 #define MOE_FLAG_KEEP_INTERMEDIATES 64u

@@ -73,7 +73,7 @@ def test_forward_rejects_null_and_small_workspace_without_gpu():
     a.x = fake
     for bad_flags in (m.FLAG_NARROW | m.FLAG_TILED, m.FLAG_NARROW | m.FLAG_TILED | m.FLAG_ONE_LAUNCH,
                       m.FLAG_ONE_KERNEL | m.FLAG_TILED, m.FLAG_ONE_KERNEL | m.FLAG_ONE_LAUNCH,
-                      # the one-kernel layer's grid barriers guard the tables its phases index with
+                      # the one-kernel layer's routing hand-off guards the tables its phases index with
                       m.FLAG_ONE_KERNEL | m.FLAG_DEBUG_SPIN_BOUND,
                       # block-FP8 weights have their own scale layout and no gate/up interleave
                       m.FLAG_WEIGHTS_FP8_BLOCK128 | m.FLAG_W13_PREINTERLEAVED,
