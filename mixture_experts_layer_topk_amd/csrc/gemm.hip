@@ -529,6 +529,10 @@ struct TileEngine {
             wait_all_but_last_issue();
         else
             wait_vmcnt<0>();
+        // the next step's loads overwrite the stage read here: its fragment
+        // reads (the late wave's are consumed only by the next step's MFMAs)
+        // complete before the barrier
+        __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));  // lgkmcnt(0)
         barrier_nofence();
     }
 
